@@ -1,0 +1,424 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+No GPU.  Every check compares the oracle with something other than itself:
+an independent construction (Sylvester doubling, explicit loops in exact
+integer arithmetic), a closed form, an invariant, an error bound, or a value
+the pages print (tests/golden/).  A plausible slip in the oracle -- a dropped
+sign flip, signs applied after the mixing, a wrong butterfly index, a
+transposed operand, a wrong zero-point sign, a wrong group index -- fails at
+least one of them (see test_planted_mistakes_are_caught).
+
+Source of the facts pinned: "Karpathy's Trick for Faster Local LLMs Finally Has
+Proper Tooling" (blog.dailydoseofds.com), sections "Why batch-one decoding is
+memory-bound" and "How Uzu optimizes bytes and tokens per pass".
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import brute
+from oracle import svg_oracle as O
+
+
+def _read_golden(path):
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+# ------------------------------------------------------------ Hadamard pins
+def test_hadamard_is_sylvester_and_orthogonal():
+    H = O.hadamard32()
+    S = np.array(brute.sylvester(32), dtype=np.int64)
+    assert np.array_equal(H, S)
+    assert set(np.unique(H)) == {-1, 1}
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H.T, 32 * np.eye(32, dtype=np.int64))
+
+
+def test_fwht_of_unit_vectors_gives_columns():
+    H = np.array(brute.sylvester(32), dtype=np.int64)
+    E = np.eye(32, dtype=np.float32)
+    U = O.fwht32(E)          # row j = transform of e_j
+    assert np.array_equal(U.T.astype(np.int64), H)
+
+
+@pytest.mark.parametrize("K", [32, 96, 256])
+def test_rotation_matches_explicit_product_on_integers(K):
+    # For |x| <= 2^10 every fp32 intermediate is an exact integer, so the
+    # fp32 oracle must equal H . diag(s) . x computed with Python ints.
+    rng = np.random.default_rng(K)
+    x = rng.integers(-1024, 1025, size=(3, K))
+    s = synth.rademacher(K, rng)
+    u = O.rht(x.astype(np.float32), s, np.float32)
+    for r in range(3):
+        ref = brute.rotate_row([int(v) for v in x[r]], [int(v) for v in s])
+        assert np.array_equal(u[r].astype(np.int64), np.array(ref, dtype=np.int64))
+
+
+def test_signs_are_applied_before_mixing():
+    # H . D . x differs from D . H . x; the pages put the sign flip first.
+    K = 32
+    x = np.arange(1, K + 1, dtype=np.float32)
+    s = np.ones(K, dtype=np.int8)
+    s[3] = -1
+    u = O.rht(x, s)
+    H = np.array(brute.sylvester(32))
+    assert np.array_equal(u, (H @ (s * x)).astype(np.float32))
+    assert not np.array_equal(u, (s * (H @ x)).astype(np.float32))
+
+
+def test_rotation_exactly_reversible_fp64():
+    # (1/32) D H (H D x) = x exactly for integer x (every step exact in fp64).
+    rng = np.random.default_rng(7)
+    K = 512
+    x = rng.integers(-2 ** 10, 2 ** 10 + 1, size=(4, K)).astype(np.float64)
+    s = synth.rademacher(K, rng)
+    u = O.rht(x, s, np.float64)
+    back = O.fwht32(u) * s.astype(np.float64) / 32.0
+    assert np.array_equal(back, x)
+
+
+def test_rotation_exact_inverse_on_fractions():
+    # Exact rational check on non-integer data: brute force with Fractions.
+    rng = np.random.default_rng(8)
+    K = 64
+    x = [Fraction(int(a), 7) for a in rng.integers(-500, 500, size=K)]
+    s = [int(v) for v in synth.rademacher(K, rng)]
+    u = brute.rotate_row(x, s)
+    back = brute.rotate_row(u, [1] * K)
+    back = [back[k] * s[k] / 32 for k in range(K)]
+    assert back == x
+    # and the fp64 oracle agrees with the exact value to rounding
+    uo = O.rht(np.array([float(v) for v in x]), np.array(s, np.int8), np.float64)
+    assert np.max(np.abs(uo - np.array([float(v) for v in u]))) < 1e-9
+
+
+@pytest.mark.parametrize("shape", [(1, 1024, 1024), (1, 4096, 512)])
+def test_rotated_product_preserved_fp64(shape):
+    M, K, N = shape
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((N, K))
+    x = rng.standard_normal((M, K))
+    s = synth.rademacher(K, rng)
+    y0 = x @ W.T
+    y1 = O.rht(x, s, np.float64) @ O.rht(W, s, np.float64).T / 32.0
+    scale = np.max(np.abs(x)) * np.max(np.abs(W)) * K
+    assert np.max(np.abs(y1 - y0)) / scale <= 1e-12
+    assert np.max(np.abs(y1 - y0)) / np.max(np.abs(y0)) <= 1e-12
+
+
+def test_outlier_spreads_to_moderate_values():
+    # One value A in a block becomes 32 values of magnitude A (A/sqrt(32)
+    # after the overall scale): max/rms drops from sqrt(32) to 1.
+    K = 64
+    A = 1000.0
+    for j in (0, 5, 31, 40):
+        x = np.zeros(K, np.float32)
+        x[j] = A
+        s = synth.rademacher(K, np.random.default_rng(j))
+        u = O.rht(x, s)
+        blk = u[(j // 32) * 32:(j // 32) * 32 + 32]
+        assert np.all(np.abs(blk) == A)
+        other = np.delete(u, np.arange((j // 32) * 32, (j // 32) * 32 + 32))
+        assert np.all(other == 0)
+        rms = math.sqrt(float(np.mean(x[(j // 32) * 32:(j // 32) * 32 + 32] ** 2)))
+        assert abs(A / rms - math.sqrt(32)) < 1e-9
+        assert abs(np.max(np.abs(blk)) / math.sqrt(float(np.mean(blk.astype(np.float64) ** 2))) - 1.0) < 1e-12
+
+
+def _dequant_w4(q, s, z, group):
+    N, K = q.shape
+    G = K // group
+    return ((q.reshape(N, G, group).astype(np.float64) - z[:, :, None].astype(np.float64))
+            * s.astype(np.float64)[:, :, None]).reshape(N, K)
+
+
+def test_rotation_lowers_w4_error_on_outliers():
+    # Statistical, seeded: weights with a few large entries quantize with lower
+    # error after the rotation (the motivation the pages give).
+    rng = np.random.default_rng(5)
+    N, K, g = 256, 1024, 32
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    idx = rng.choice(N * K, size=N * K // 200, replace=False)
+    W.reshape(-1)[idx] *= 50
+    s = synth.rademacher(K, rng)
+    q, sc, z = O.quant_w4(W, g)
+    err_plain = np.mean((_dequant_w4(q, sc, z, g) - W) ** 2)
+    u = O.rht(W, s)
+    q2, sc2, z2 = O.quant_w4(u, g)
+    err_rot = np.mean((_dequant_w4(q2, sc2, z2, g) - u) ** 2) / 32.0  # back to W's scale
+    assert err_rot < 0.8 * err_plain
+
+
+# ---------------------------------------------------------- quantizer pins
+def test_act_quant_bounds_and_extremes():
+    x, W, signs, spec = synth.single_inputs("single_1k")
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([x, rng.standard_t(3, size=(5, 1024)).astype(np.float32),
+                           -np.abs(rng.standard_normal((1, 1024))).astype(np.float32)])
+    u = O.rht(rows, signs)
+    q, sc = O.act_quant_i8(u)
+    assert q.dtype == np.int8 and sc.dtype == np.float32
+    sigma = sc.astype(np.float64) * 32.0          # the quantization step
+    for m in range(u.shape[0]):
+        assert np.max(np.abs(q[m])) == 127
+        assert abs(int(q[m, np.argmax(np.abs(u[m]))])) == 127
+        assert np.all(q[m] >= -127)
+        # round-to-nearest: error at most half a step (plus fp32 slack)
+        err = np.abs(u[m].astype(np.float64) - sigma[m] * q[m])
+        assert np.max(err) <= sigma[m] * (0.5 + 1e-5)
+        # the step is amax/127 to fp32 precision
+        assert abs(sigma[m] - np.max(np.abs(u[m])) / 127.0) <= 2e-7 * sigma[m]
+        # signs of the codes follow the values
+        assert np.all(np.sign(q[m][np.abs(u[m]) > sigma[m]]) == np.sign(u[m][np.abs(u[m]) > sigma[m]]))
+
+
+def test_act_quant_zero_row():
+    q, sc = O.act_quant_i8(np.zeros((2, 64), np.float32))
+    assert not q.any() and not sc.any()
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_w4_quant_bounds(group):
+    rng = np.random.default_rng(group)
+    N, K = 64, 512
+    u = (rng.standard_normal((N, K)) * 0.5).astype(np.float32)
+    u[0, :group] = np.abs(u[0, :group])        # all-positive group: lo = 0
+    u[1, :group] = -np.abs(u[1, :group])       # all-negative group: hi = 0
+    u[2, :group] = 0.0                         # zero group
+    q, s, z = O.quant_w4(u, group)
+    assert q.max() <= 15 and z.max() <= 15
+    G = K // group
+    ug = u.reshape(N, G, group).astype(np.float64)
+    lo = np.minimum(0, ug.min(-1))
+    hi = np.maximum(0, ug.max(-1))
+    s64 = s.astype(np.float64)
+    nz = hi > lo
+    # s is (hi - lo)/15 to fp16 precision
+    assert np.all(np.abs(s64[nz] - (hi - lo)[nz] / 15) <= (2.0 ** -11) * s64[nz] * 1.001)
+    assert np.all(s64[~nz] == 1.0)
+    # every value within half a step (tiny slack: fp16 scale rounding at the top)
+    rec = _dequant_w4(q, s, z, group).reshape(N, G, group)
+    err = np.abs(rec - ug)
+    assert np.all(err <= s64[:, :, None] * (0.5 + 16 * 2.0 ** -11))
+    assert np.all(rec[2, 0] == 0) and z[0, 0] == 0 and z[1, 0] == 15
+    # zero is represented exactly
+    assert np.all(np.abs(-z.astype(np.float64) * s64 + z * s64) == 0)
+
+
+def test_w8_quant_bounds():
+    rng = np.random.default_rng(2)
+    u = rng.standard_t(3, size=(32, 384)).astype(np.float32)
+    u[3] = 0
+    q, s = O.quant_w8(u)
+    s64 = s.astype(np.float64)
+    assert s64[3] == 1.0 and not q[3].any()
+    err = np.abs(u.astype(np.float64) - s64[:, None] * q)
+    assert np.all(err <= s64[:, None] * (0.5 + 2.0 ** -10))
+    assert np.all(np.abs(q) <= 127)
+    a = np.max(np.abs(u.astype(np.float64)), axis=1)
+    ok = a > 0
+    assert np.all(np.abs(s64[ok] - a[ok] / 127) <= 2.0 ** -11 * s64[ok] * 1.001)
+
+
+def test_pack_layout_by_hand():
+    q = np.array([[1, 2, 3, 4, 15, 0, 7, 8]], dtype=np.uint8)
+    assert O.pack_w4_codes(q).tolist() == [[0x21, 0x43, 0x0F, 0x87]]
+    z = np.array([[3, 12, 5]], dtype=np.uint8)
+    assert O.pack_z4(z).tolist() == [[0xC3, 0x05]]
+
+
+# ------------------------------------------------------- contraction pins
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_w4_partials_match_brute_force(group):
+    rng = np.random.default_rng(100 + group)
+    M, N, K = 2, 3, 256
+    qx = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    z = rng.integers(0, 16, size=(N, K // group)).astype(np.uint8)
+    S = O.w4_group_partials(qx, qw, z, group)
+    ref = brute.w4_partials(qx.tolist(), qw.tolist(), z.tolist(), group)
+    assert np.array_equal(S, np.array(ref, dtype=np.int64))
+
+
+def test_w8_partials_match_brute_force():
+    rng = np.random.default_rng(4)
+    qx = rng.integers(-127, 128, size=(2, 96)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(4, 96)).astype(np.int8)
+    assert np.array_equal(O.w8_partials(qx, qw), np.array(brute.w8_partials(qx.tolist(), qw.tolist())))
+
+
+def test_partial_bounds_extremes():
+    # |S_g| <= 127 * 15 * g for W4 and |S| <= 127^2 K for W8, attained.
+    g = 128
+    qx = np.full((1, g), 127, np.int8)
+    qw = np.full((1, g), 15, np.uint8)
+    z = np.zeros((1, 1), np.uint8)
+    assert O.w4_group_partials(qx, qw, z, g)[0, 0, 0] == 127 * 15 * g
+    assert O.w4_group_partials(-qx, qw, z, g)[0, 0, 0] == -127 * 15 * g
+    K = 12288
+    S = O.w8_partials(np.full((1, K), -127, np.int8), np.full((1, K), 127, np.int8))
+    assert S[0, 0] == -127 * 127 * K and abs(S[0, 0]) < 2 ** 31
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_output_equals_dequantized_product(group):
+    # y_ref must equal the fp64 product of the dequantized operands:
+    # sum_k (x_scale q_x)(s (q_w - z)); computed here by dequantize + matmul.
+    x, W, signs = synth.random_case(3, 48, 512, seed=group)
+    w = O.prepare_w4(W, signs, group)
+    y, S, qx, sx = O.linear_w4(x, signs, w)
+    xd = sx.astype(np.float64)[:, None] * qx.astype(np.float64)
+    wd = _dequant_w4(w["q"], w["s"], w["z"], group)
+    y2 = xd @ wd.T
+    assert np.max(np.abs(y - y2)) <= 1e-12 * np.max(np.abs(y2))
+
+
+def test_w8_output_equals_dequantized_product():
+    x, W, signs = synth.random_case(4, 40, 384, seed=9)
+    w = O.prepare_w8(W, signs)
+    y, S, qx, sx = O.linear_w8(x, signs, w)
+    y2 = (sx.astype(np.float64)[:, None] * qx) @ (w["s"].astype(np.float64)[:, None] * w["q"]).T
+    assert np.max(np.abs(y - y2)) <= 1e-12 * np.max(np.abs(y2))
+
+
+@pytest.mark.parametrize("fmt", ["w4", "w8"])
+def test_quantized_layer_tracks_fp64_product(fmt):
+    # The encoding changes the product only by quantization error: a quality
+    # check against the unquantized fp64 W x (not a parity gate).
+    x, W, signs, spec = synth.single_inputs("single_1k")
+    y_true = x.astype(np.float64) @ W.astype(np.float64).T
+    if fmt == "w4":
+        y, *_ = O.linear_w4(x, signs, O.prepare_w4(W, signs, 32))
+        tol = 0.15
+    else:
+        y, *_ = O.linear_w8(x, signs, O.prepare_w8(W, signs))
+        tol = 0.02
+    rel = np.linalg.norm(y - y_true) / np.linalg.norm(y_true)
+    assert rel < tol, rel
+
+
+# ---------------------------------------------------------- byte accounting
+def test_byte_ceiling_worked_example(golden_dir):
+    g = _read_golden(os.path.join(golden_dir, "byte_ceiling.txt"))
+    p = O.passes_per_second(g["bandwidth_bytes_per_s"], g["bytes_per_pass"])
+    assert round(p) == g["ceiling_per_s_rounded"]
+    assert abs(p - 29.423) < 1e-3
+
+
+@pytest.mark.parametrize("fmt,group", [("w4_z4", 32), ("w4_z16", 64), ("w4_z16", 128), ("w8", 0)])
+def test_linear_bytes_counts_real_arrays(fmt, group):
+    M, N, K = 5, 24, 384
+    x, W, signs = synth.random_case(M, N, K, seed=1)
+    if fmt == "w8":
+        w = O.prepare_w8(W, signs)
+        wbytes = w["q"].nbytes + w["s"].nbytes
+    else:
+        w = O.prepare_w4(W, signs, group)
+        z = O.pack_z4(w["z"]) if fmt == "w4_z4" else O.zeros_as_f16(w["z"])
+        wbytes = O.pack_w4_codes(w["q"]).nbytes + w["s"].nbytes + z.nbytes
+    qx, sx = O.quant_acts(x, signs)
+    y = np.zeros((M, N), np.float32)
+    assert O.linear_bytes(M, N, K, fmt, group) == wbytes + qx.nbytes + sx.nbytes + y.nbytes
+
+
+def test_plain_decoding_is_one_token_per_pass(golden_dir):
+    g = _read_golden(os.path.join(golden_dir, "tokens_per_pass.txt"))
+    assert g["plain_decoding_tokens_per_pass"] == 1.0
+    assert g["draft_advance"] == g["draft_agreed_prefix"] + 1
+
+
+def test_output_error_metric():
+    y_ref = np.array([[1.0, -2.0, 1e-6, 0.0]])
+    e, r, ex = O.output_error(y_ref * (1 + 1e-3), y_ref)
+    assert abs(e - 1e-3) < 1e-9 and ex == 2
+    e, r, ex = O.output_error(y_ref + np.array([[0, 0, 0, 4e-3]]), y_ref)
+    assert e == 0 and abs(r - 2e-3) < 1e-12
+
+
+# ------------------------------------------------- planted-mistake check
+def test_planted_mistakes_are_caught(monkeypatch):
+    """Plant plausible slips in the oracle (on the CPU) and check that the
+    pins above reject each one."""
+    def fwht_wrong_sign(v):
+        v = np.array(v, copy=True)
+        b = v.reshape(-1, v.shape[-1] // 32, 32)
+        for h in (1, 2, 4, 8, 16):
+            lo = [i for i in range(32) if not i & h]
+            hi = [i + h for i in lo]
+            a, c = b[:, :, lo], b[:, :, hi]
+            b[:, :, lo] = a + c
+            b[:, :, hi] = c - a          # slip: reversed difference
+        return b.reshape(v.shape)
+
+    def rht_signs_after(r, signs, dtype=np.float32):
+        return O.fwht32(np.asarray(r, dtype)) * np.asarray(signs).astype(dtype)
+
+    def partials_wrong_zero(qx, q, z, group):
+        M, K = qx.shape
+        N = q.shape[0]
+        G = K // group
+        xg = qx.astype(np.int64).reshape(M, G, group)
+        wg = q.astype(np.int64).reshape(N, G, group) + z.astype(np.int64)[:, :, None]
+        return np.einsum("mjk,njk->mnj", xg, wg)
+
+    _orig_partials = O.w4_group_partials
+
+    def partials_shifted_group(qx, q, z, group):
+        return _orig_partials(qx, q, np.roll(z, 1, axis=1), group)  # slip: wrong group index
+
+    def act_quant_signed_max(u):
+        u = np.asarray(u, np.float32)
+        amax = np.max(u, axis=-1)                                  # slip: max, not max |u|
+        sigma = amax / np.float32(127)
+        q = np.clip(np.rint(u / sigma[..., None]), -127, 127).astype(np.int8)
+        return q, (sigma * np.float32(2.0 ** -5)).astype(np.float32)
+
+    _orig_w4 = O.quant_w4
+
+    def quant_w4_zero_sign(u, group):
+        q, s, z = _orig_w4(u, group)
+        N, K = q.shape
+        zz = np.repeat(z, group, axis=1)
+        q2 = np.clip(q.astype(np.int32) - 2 * zz.astype(np.int32), 0, 15)  # slip: u/s - z
+        return q2.astype(np.uint8), s, z
+
+    caught = []
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "fwht32", fwht_wrong_sign)
+        caught.append(_fails(test_fwht_of_unit_vectors_gives_columns))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "rht", rht_signs_after)
+        caught.append(_fails(lambda: test_rotation_matches_explicit_product_on_integers(96)))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "w4_group_partials", partials_wrong_zero)
+        caught.append(_fails(lambda: test_w4_partials_match_brute_force(64)))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "w4_group_partials", partials_shifted_group)
+        caught.append(_fails(lambda: test_w4_partials_match_brute_force(32)))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "act_quant_i8", act_quant_signed_max)
+        caught.append(_fails(test_act_quant_bounds_and_extremes))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "quant_w4", quant_w4_zero_sign)
+        caught.append(_fails(lambda: test_w4_quant_bounds(64)))
+    assert all(caught), caught
+
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
