@@ -1,0 +1,164 @@
+/*
+ * svgemm.h -- C ABI of the MI355X (gfx950) RHT + W4A8 / W8A8 quantized linear.
+ *
+ * Sources.  [KT] is the page "Karpathy's Trick for Faster Local LLMs Finally
+ * Has Proper Tooling" (blog.dailydoseofds.com).  The three operations follow
+ * its section "How Uzu optimizes bytes and tokens per pass": weights are
+ * rotated by a block-diagonal random Hadamard transform (random sign flips,
+ * then a +/-1 Hadamard on each block of 32) and quantized as 4-bit asymmetric
+ * ("Medium") or 8-bit symmetric ("Large") integers; activations are rotated
+ * the same way and quantized to int8 on the fly; the matmul is integer x
+ * integer.  Its section "Producing several tokens from one model pass" sets the
+ * verify sizes (16 to 32 candidate rows instead of 1).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is a DEVICE pointer; the caller owns all memory.  Nothing
+ *    is allocated, freed or synchronised inside a call.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream).  They may be captured in a HIP graph: no call records
+ *    a memset or a host round trip.
+ *  - Arguments are validated on the host before anything is enqueued; a failed
+ *    check returns its status, sets svg_last_error(), and leaves every output
+ *    untouched.  M == 0 or N == 0 is a valid empty call (nothing enqueued).
+ *  - Outputs are overwritten, never accumulated.  Inputs and outputs must not
+ *    overlap.
+ *  - Numerics: the transform and every quantizer use IEEE fp32 add, subtract
+ *    and divide with round-to-nearest-even and no fused multiply-add, so the
+ *    integer codes are reproducible bit for bit; NaN/Inf inputs are outside
+ *    the contract.
+ *
+ * The rotation is unnormalised (entries +/-1); the overall scale of the
+ * transform on both operands, 1/sqrt(32) twice = 2^-5, is folded exactly into
+ * x_scale.  One Hadamard ordering is used throughout: Sylvester natural order,
+ * H[i][j] = (-1)^popcount(i & j).
+ */
+#ifndef SVGEMM_H
+#define SVGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int svg_status;
+
+enum {
+    SVG_OK = 0,
+    SVG_EINVAL = 1,        /* null required pointer, negative size, K <= 0      */
+    SVG_EUNSUPPORTED = 2,  /* block != 32, K % 32, K % group, group not in
+                              {32, 64, 128}, M > 32, unknown fmt, W8 K > 131072 */
+    SVG_EALIGN = 3,        /* a pointer below its required alignment          */
+    SVG_EHIP = 4           /* a HIP launch or runtime error (text in
+                              svg_last_error())                               */
+};
+
+enum {
+    SVG_W4_ASYM_Z4 = 0,   /* codes u8 [N][K/2]; scale fp16 [N][K/g];
+                             zero u4 packed two per byte [N][(K/g + 1)/2]     */
+    SVG_W4_ASYM_Z16 = 1,  /* codes u8 [N][K/2]; scale fp16 [N][K/g];
+                             zero fp16 (integer 0..15) [N][K/g]               */
+    SVG_W8_SYM = 2        /* codes i8 [N][K]; scale fp16 [N]; no zero          */
+};
+
+/*
+ * rht_rotate_weights -- offline: rotate and quantize the rows of W.
+ * [KT "How Uzu optimizes bytes and tokens per pass": the transform is applied
+ *  before quantization; Medium = 4-bit asymmetric, Large = 8-bit symmetric.]
+ *
+ *  W        fp32 [N][K] row-major; row n is output channel n, contiguous in K.
+ *           16-byte aligned.
+ *  signs    int8 [K], each +1 or -1; the same vector must be given to
+ *           act_rht_quant_i8 for the activations this matrix consumes.
+ *           4-byte aligned.
+ *  block    transform block; must be 32.
+ *  fmt      SVG_W4_ASYM_Z4, SVG_W4_ASYM_Z16 or SVG_W8_SYM.
+ *  group    W4: quantization group along K, 32, 64 or 128 (independent of the
+ *           transform block).  Ignored for W8.
+ *  wq       W4: u8 [N][K/2], byte j of a row holds code k=2j in its low nibble
+ *           and k=2j+1 in its high nibble; W8: i8 [N][K].  16-byte aligned.
+ *  w_scale  fp16 bits; W4: [N][K/group]; W8: [N].  2-byte aligned.
+ *  w_zero   W4 Z4: u8 [N][(K/group + 1)/2], group 2j in the low nibble;
+ *           W4 Z16: fp16 bits [N][K/group], integer values 0..15;
+ *           W8: unused, may be NULL.
+ *  w_rot_debug  nullable fp32 [N][K]: receives the rotated rows u (tests).
+ *
+ *  Per row, u = H_32 . diag(signs) . W[n] blockwise (butterfly stages
+ *  h = 1, 2, 4, 8, 16 in that order).  W4 per group: lo = min(0, min u),
+ *  hi = max(0, max u), s = fp16(rne((hi - lo) / 15)) (1.0 if zero),
+ *  z = rint(-lo / s), q = clamp(rint(u / s) + z, 0, 15).  W8 per row:
+ *  s = fp16(rne(max|u| / 127)) (1.0 if zero), q = clamp(rint(u / s), -127, 127).
+ */
+svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
+                              int block, int fmt, int group, void* wq,
+                              uint16_t* w_scale, void* w_zero, float* w_rot_debug,
+                              void* stream);
+
+/*
+ * act_rht_quant_i8 -- online: rotate the activation rows and quantize each to
+ * int8 with one scale per row (token).
+ * [KT "How Uzu optimizes bytes and tokens per pass": activations are quantized
+ *  to 8 bits on the fly.]
+ *
+ *  X        fp32 [M][K] row-major, 16-byte aligned.  M <= 32.
+ *  signs    int8 [K] (+/-1), 4-byte aligned; the weights' sign vector.
+ *  block    must be 32.
+ *  xq       int8 [M][K] codes in [-127, 127], 16-byte aligned.
+ *  x_scale  fp32 [M]: (max_k |u| / 127) * 2^-5 (0 for an all-zero row); 4-byte
+ *           aligned.
+ *
+ *  u = H_32 . diag(signs) . X[m] blockwise; sigma = max|u| / 127;
+ *  q = clamp(rint(u / sigma), -127, 127) (0 if the row is zero).
+ */
+svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs,
+                            int block, int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * w4a8_linear -- y = x . W^T for int8 activations and W4 asymmetric weights.
+ * [KT "How Uzu optimizes bytes and tokens per pass": both operands are
+ *  integers and the product runs on the int8 matrix path; "Why batch-one
+ *  decoding is memory-bound": each pass streams every weight once.]
+ *
+ *  xq, x_scale   from act_rht_quant_i8 (xq 16-byte aligned), M in 1..32.
+ *  wq, w_scale, w_zero, fmt (SVG_W4_ASYM_Z4 or _Z16), group: from
+ *                rht_rotate_weights with the same signs, N rows, K columns.
+ *  y             fp32 [M][N], 4-byte aligned.
+ *  partials_debug  nullable int32 [M][N][K/group]: receives
+ *                S_g[m][n] = sum_{k in g} xq[m][k] * (q[n][k] - z[n][g]),
+ *                exact (tests).
+ *
+ *  y[m][n] = x_scale[m] * sum_g s[n][g] * S_g[m][n]  (fp32 accumulation; the
+ *  integer partial sums are exact, the float sum is order-dependent only).
+ */
+svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
+                       const uint8_t* wq, const uint16_t* w_scale, const void* w_zero,
+                       int fmt, int group, int N, float* y, int32_t* partials_debug,
+                       void* stream);
+
+/*
+ * w8a8_linear -- y = x . W^T for int8 activations and W8 symmetric weights.
+ * [KT "How Uzu optimizes bytes and tokens per pass": Large checkpoints are
+ *  8-bit symmetric; both operands are integers.]
+ *
+ *  xq, x_scale   from act_rht_quant_i8 (xq 16-byte aligned), M in 1..32.
+ *  wq            int8 [N][K] from rht_rotate_weights (SVG_W8_SYM), 16-byte
+ *                aligned; w_scale fp16 bits [N].  K <= 131072 (so that
+ *                |S| <= 127^2 K fits int32).
+ *  y             fp32 [M][N].
+ *  partials_debug  nullable int32 [M][N]: S[m][n] = sum_k xq[m][k] * q[n][k].
+ *
+ *  y[m][n] = x_scale[m] * s[n] * S[m][n].
+ */
+svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
+                       const int8_t* wq, const uint16_t* w_scale, int N, float* y,
+                       int32_t* partials_debug, void* stream);
+
+/* Text of the last error on the calling thread ("" after a successful call);
+ * valid until the next call on this thread. */
+const char* svg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVGEMM_H */

@@ -1,0 +1,190 @@
+"""Python binding of libsvgemm (the MI355X RHT + W4A8 / W8A8 quantized linear).
+
+Argument marshalling only: every function checks tensor devices, dtypes and
+shapes, derives the sizes, and calls the C entry point of the same name in
+libsvgemm.so on the current HIP stream (or the one given).  All computation
+runs in the library's HIP kernels; there is no Python or CPU fallback, and
+importing this module fails if the library has not been built
+(``python -m speculative_verify_gemm_amd.build``).
+
+The operations follow the page "Karpathy's Trick for Faster Local LLMs Finally
+Has Proper Tooling" (blog.dailydoseofds.com), section "How Uzu optimizes bytes
+and tokens per pass": rotate the weights (random sign flips, then a 32-wide
++/-1 Hadamard per block) and quantize them as 4-bit asymmetric or 8-bit
+symmetric integers; rotate and quantize the activations to int8 on the fly;
+multiply integer by integer.  Layouts and numerics are those of
+include/svgemm.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvgemm.so")
+
+SVG_OK, SVG_EINVAL, SVG_EUNSUPPORTED, SVG_EALIGN, SVG_EHIP = 0, 1, 2, 3, 4
+W4_Z4, W4_Z16, W8 = 0, 1, 2
+FORMATS = {"w4_z4": W4_Z4, "w4_z16": W4_Z16, "w8": W8}
+BLOCK = 32
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m speculative_verify_gemm_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.rht_rotate_weights.argtypes = [vp, i, i, vp, i, i, i, vp, vp, vp, vp, vp]
+    lib.act_rht_quant_i8.argtypes = [vp, i, i, vp, i, vp, vp, vp]
+    lib.w4a8_linear.argtypes = [vp, vp, i, i, vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.w8a8_linear.argtypes = [vp, vp, i, i, vp, vp, i, vp, vp, vp]
+    for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear):
+        fn.restype = ctypes.c_int
+    lib.svg_last_error.argtypes = []
+    lib.svg_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class SvgError(RuntimeError):
+    """A non-zero status from libsvgemm."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libsvgemm status {status}: {message}")
+        self.status = status
+
+
+def last_error() -> str:
+    return lib.svg_last_error().decode()
+
+
+def _check(status: int):
+    if status != SVG_OK:
+        raise SvgError(status, last_error())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream, t):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+# ------------------------------------------------------------ entry points
+def rht_rotate_weights(W, signs, fmt, group, wq, w_scale, w_zero=None, w_rot_debug=None,
+                       block=BLOCK, stream=None):
+    """Rotate and quantize fp32 weights W[N, K] into (wq, w_scale, w_zero)."""
+    f = _fmt(fmt)
+    _dev(W, "W", torch.float32)
+    _dev(signs, "signs", torch.int8)
+    N, K = W.shape
+    if f == W8:
+        _dev(wq, "wq", torch.int8)
+        if tuple(wq.shape) != (N, K) or tuple(w_scale.shape) != (N,):
+            raise ValueError("W8 expects wq [N, K] and w_scale [N]")
+    else:
+        _dev(wq, "wq", torch.uint8)
+        G = K // group
+        zshape = (N, (G + 1) // 2) if f == W4_Z4 else (N, G)
+        if tuple(wq.shape) != (N, K // 2) or tuple(w_scale.shape) != (N, G) or \
+                w_zero is None or tuple(w_zero.shape) != zshape:
+            raise ValueError("W4 expects wq [N, K/2], w_scale [N, K/g], w_zero "
+                             f"{zshape}")
+        _dev(w_zero, "w_zero", torch.uint8 if f == W4_Z4 else torch.float16)
+    _dev(w_scale, "w_scale", torch.float16)
+    if w_rot_debug is not None:
+        _dev(w_rot_debug, "w_rot_debug", torch.float32)
+    _check(lib.rht_rotate_weights(_p(W), N, K, _p(signs), block, f, group, _p(wq), _p(w_scale),
+                                  _p(w_zero), _p(w_rot_debug), _stream(stream, W)))
+
+
+def act_rht_quant_i8(X, signs, xq, x_scale, block=BLOCK, stream=None):
+    """Rotate fp32 activations X[M, K] and quantize each row to int8."""
+    _dev(X, "X", torch.float32)
+    _dev(signs, "signs", torch.int8)
+    _dev(xq, "xq", torch.int8)
+    _dev(x_scale, "x_scale", torch.float32)
+    M, K = X.shape
+    if tuple(xq.shape) != (M, K) or tuple(x_scale.shape) != (M,):
+        raise ValueError("xq must be [M, K] and x_scale [M]")
+    _check(lib.act_rht_quant_i8(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale),
+                                _stream(stream, X)))
+
+
+def w4a8_linear(xq, x_scale, wq, w_scale, w_zero, fmt, group, y, partials_debug=None,
+                stream=None):
+    """y[M, N] = dequantized (xq . W^T) for W4 weights."""
+    f = _fmt(fmt)
+    _dev(xq, "xq", torch.int8)
+    _dev(x_scale, "x_scale", torch.float32)
+    _dev(wq, "wq", torch.uint8)
+    _dev(w_scale, "w_scale", torch.float16)
+    _dev(w_zero, "w_zero", torch.uint8 if f == W4_Z4 else torch.float16)
+    _dev(y, "y", torch.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K or tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch between xq, wq and y")
+    if partials_debug is not None:
+        _dev(partials_debug, "partials_debug", torch.int32)
+        if tuple(partials_debug.shape) != (M, N, K // group):
+            raise ValueError("partials_debug must be [M, N, K/g]")
+    _check(lib.w4a8_linear(_p(xq), _p(x_scale), M, K, _p(wq), _p(w_scale), _p(w_zero), f, group,
+                           N, _p(y), _p(partials_debug), _stream(stream, xq)))
+
+
+def w8a8_linear(xq, x_scale, wq, w_scale, y, partials_debug=None, stream=None):
+    """y[M, N] = dequantized (xq . W^T) for W8 weights."""
+    _dev(xq, "xq", torch.int8)
+    _dev(x_scale, "x_scale", torch.float32)
+    _dev(wq, "wq", torch.int8)
+    _dev(w_scale, "w_scale", torch.float16)
+    _dev(y, "y", torch.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch between xq, wq and y")
+    if partials_debug is not None:
+        _dev(partials_debug, "partials_debug", torch.int32)
+        if tuple(partials_debug.shape) != (M, N):
+            raise ValueError("partials_debug must be [M, N]")
+    _check(lib.w8a8_linear(_p(xq), _p(x_scale), M, K, _p(wq), _p(w_scale), N, _p(y),
+                           _p(partials_debug), _stream(stream, xq)))
+
+
+# ------------------------------------------------------------- allocation
+def empty_weights(N, K, fmt, group, device="cuda"):
+    """Uninitialised output buffers for rht_rotate_weights: (wq, w_scale, w_zero)."""
+    f = _fmt(fmt)
+    if f == W8:
+        return (torch.empty((N, K), dtype=torch.int8, device=device),
+                torch.empty((N,), dtype=torch.float16, device=device), None)
+    G = K // group
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
+    sc = torch.empty((N, G), dtype=torch.float16, device=device)
+    if f == W4_Z4:
+        z = torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=device)
+    else:
+        z = torch.empty((N, G), dtype=torch.float16, device=device)
+    return wq, sc, z

@@ -1,0 +1,259 @@
+// Block-diagonal random Hadamard transform fused with quantization, gfx950.
+//
+//  * k_act_rht_quant   -- activations: sign flip + 32-wide butterfly, per-row
+//                         |u| max, int8 codes and the per-row scale.
+//  * k_rot_quant_w4    -- weights, 4-bit asymmetric per group along K.
+//  * k_rot_quant_w8    -- weights, 8-bit symmetric per row.
+//
+// Source: "Karpathy's Trick for Faster Local LLMs Finally Has Proper Tooling"
+// (blog.dailydoseofds.com), section "How Uzu optimizes bytes and tokens per
+// pass": random sign flips come before the mixing, each block of 32 values is
+// mixed on its own by a +/-1 Hadamard, the transform precedes quantization,
+// activations are quantized to 8 bits on the fly, Medium weights are 4-bit
+// asymmetric and Large weights 8-bit symmetric.
+//
+// Mapping: a 256-thread workgroup owns one row.  Each thread holds one float4
+// (4 consecutive values), so a 32-block spans 8 consecutive lanes and the
+// butterfly needs only lane exchanges (DPP and ds_swizzle), no LDS traffic.
+// Row-wide maxima use two passes over the row (the second pass recomputes the
+// transform from the L2-resident input, which is bit-identical), so any K is
+// handled without holding the row in registers.
+//
+// Everything that decides an integer code is one IEEE fp32 operation with
+// round-to-nearest-even (this file is compiled with -ffp-contract=off and
+// correctly rounded division): the codes match a plain fp32 implementation of
+// the same steps bit for bit.
+#include "svg_device.h"
+#include "svg_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Load 4 values and their 4 signs, flip and transform.  `valid` is uniform
+// over each 8-lane block because K is a multiple of 32.
+SVG_DEV void rotate_chunk(const float* __restrict__ row, const int8_t* __restrict__ signs, int c,
+                          bool valid, float& e0, float& e1, float& e2, float& e3) {
+  if (valid) {
+    const float4 v = *reinterpret_cast<const float4*>(row + 4 * c);
+    const int sg = *reinterpret_cast<const int*>(signs + 4 * c);
+    e0 = v.x; e1 = v.y; e2 = v.z; e3 = v.w;
+    apply_signs4(e0, e1, e2, e3, sg);
+  } else {
+    e0 = e1 = e2 = e3 = 0.f;
+  }
+  fwht32_lane4(e0, e1, e2, e3);
+}
+
+// Max over the workgroup (exact: max is order-free).
+SVG_DEV float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+SVG_DEV int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+#pragma clang fp contract(off)
+
+__global__ __launch_bounds__(kThreads) void k_act_rht_quant(const float* __restrict__ X, int K,
+                                                           const int8_t* __restrict__ signs,
+                                                           int8_t* __restrict__ xq,
+                                                           float* __restrict__ x_scale) {
+  __shared__ float red[kThreads / 64];
+  const int m = blockIdx.x;
+  const float* row = X + (size_t)m * K;
+  const int nchunk = K >> 2;
+  float amax = 0.f;
+  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const bool valid = c < nchunk;
+    float e0, e1, e2, e3;
+    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    if (valid) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0), fabsf(e1)), fmaxf(fabsf(e2), fabsf(e3))));
+  }
+  amax = block_max(amax, red);
+  const float sigma = amax / 127.0f;
+  if (threadIdx.x == 0) x_scale[m] = sigma * 0.03125f;  // exact: carries the transform's 2^-5
+  int8_t* out = xq + (size_t)m * K;
+  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const bool valid = c < nchunk;
+    float e0, e1, e2, e3;
+    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    if (valid) {
+      int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+      if (amax > 0.f) {
+        q0 = clamp_i((int)rintf(e0 / sigma), -127, 127);
+        q1 = clamp_i((int)rintf(e1 / sigma), -127, 127);
+        q2 = clamp_i((int)rintf(e2 / sigma), -127, 127);
+        q3 = clamp_i((int)rintf(e3 / sigma), -127, 127);
+      }
+      const u32 packed = (u32)(q0 & 0xFF) | ((u32)(q1 & 0xFF) << 8) | ((u32)(q2 & 0xFF) << 16) |
+                         ((u32)(q3 & 0xFF) << 24);
+      *reinterpret_cast<u32*>(out + 4 * c) = packed;
+    }
+  }
+}
+
+// Group-wise min/max over the LPG = G/4 lanes that hold one quantization group.
+template <int LPG>
+SVG_DEV float group_min(float v) {
+  v = fminf(v, lane_xorf<1>(v));
+  v = fminf(v, lane_xorf<2>(v));
+  v = fminf(v, lane_xorf<4>(v));
+  if constexpr (LPG >= 16) v = fminf(v, lane_xorf<8>(v));
+  if constexpr (LPG >= 32) v = fminf(v, lane_xorf<16>(v));
+  return v;
+}
+template <int LPG>
+SVG_DEV float group_max(float v) {
+  v = fmaxf(v, lane_xorf<1>(v));
+  v = fmaxf(v, lane_xorf<2>(v));
+  v = fmaxf(v, lane_xorf<4>(v));
+  if constexpr (LPG >= 16) v = fmaxf(v, lane_xorf<8>(v));
+  if constexpr (LPG >= 32) v = fmaxf(v, lane_xorf<16>(v));
+  return v;
+}
+
+template <int G, bool Z4>
+__global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restrict__ W, int K,
+                                                          const int8_t* __restrict__ signs,
+                                                          uint8_t* __restrict__ wq,
+                                                          uint16_t* __restrict__ w_scale,
+                                                          void* __restrict__ w_zero,
+                                                          float* __restrict__ w_rot) {
+  constexpr int LPG = G / 4;  // lanes per group (8, 16 or 32)
+  const int n = blockIdx.x;
+  const float* row = W + (size_t)n * K;
+  const int nchunk = K >> 2;
+  const int NG = K / G;
+  const int lane = threadIdx.x & 63;
+  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const bool valid = c < nchunk;  // uniform over each group since K % G == 0
+    float e0, e1, e2, e3;
+    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    if (w_rot != nullptr && valid)
+      *reinterpret_cast<float4*>(w_rot + (size_t)n * K + 4 * c) = make_float4(e0, e1, e2, e3);
+    const float mn = group_min<LPG>(fminf(fminf(e0, e1), fminf(e2, e3)));
+    const float mx = group_max<LPG>(fmaxf(fmaxf(e0, e1), fmaxf(e2, e3)));
+    const float lo = fminf(0.f, mn);
+    const float hi = fmaxf(0.f, mx);
+    __half sh = __float2half_rn((hi - lo) / 15.0f);
+    if (__half_as_ushort(sh) == 0) sh = __ushort_as_half(0x3C00);  // 1.0
+    const float s = __half2float(sh);
+    const int z = valid ? (int)rintf(-lo / s) : 0;
+    const int q0 = clamp_i((int)rintf(e0 / s) + z, 0, 15);
+    const int q1 = clamp_i((int)rintf(e1 / s) + z, 0, 15);
+    const int q2 = clamp_i((int)rintf(e2 / s) + z, 0, 15);
+    const int q3 = clamp_i((int)rintf(e3 / s) + z, 0, 15);
+    const int gi = c / LPG;
+    const bool leader = (lane % LPG) == 0;
+    int z_next = 0;
+    if constexpr (Z4) z_next = lane_xor<LPG>(z);  // zero of the odd partner group
+    if (valid) {
+      const uint16_t packed = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
+      reinterpret_cast<uint16_t*>(wq + (size_t)n * (K >> 1))[c] = packed;
+      if (leader) {
+        w_scale[(size_t)n * NG + gi] = __half_as_ushort(sh);
+        if constexpr (Z4) {
+          if ((gi & 1) == 0) {
+            const int zo = (gi + 1 < NG) ? z_next : 0;
+            reinterpret_cast<uint8_t*>(w_zero)[(size_t)n * ((NG + 1) >> 1) + (gi >> 1)] =
+                (uint8_t)(z | (zo << 4));
+          }
+        } else {
+          reinterpret_cast<uint16_t*>(w_zero)[(size_t)n * NG + gi] =
+              __half_as_ushort(__int2half_rn(z));
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restrict__ W, int K,
+                                                          const int8_t* __restrict__ signs,
+                                                          int8_t* __restrict__ wq,
+                                                          uint16_t* __restrict__ w_scale,
+                                                          float* __restrict__ w_rot) {
+  __shared__ float red[kThreads / 64];
+  const int n = blockIdx.x;
+  const float* row = W + (size_t)n * K;
+  const int nchunk = K >> 2;
+  float amax = 0.f;
+  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const bool valid = c < nchunk;
+    float e0, e1, e2, e3;
+    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    if (valid) {
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0), fabsf(e1)), fmaxf(fabsf(e2), fabsf(e3))));
+      if (w_rot != nullptr)
+        *reinterpret_cast<float4*>(w_rot + (size_t)n * K + 4 * c) = make_float4(e0, e1, e2, e3);
+    }
+  }
+  amax = block_max(amax, red);
+  __half sh = __float2half_rn(amax / 127.0f);
+  if (__half_as_ushort(sh) == 0) sh = __ushort_as_half(0x3C00);
+  const float s = __half2float(sh);
+  if (threadIdx.x == 0) w_scale[n] = __half_as_ushort(sh);
+  int8_t* out = wq + (size_t)n * K;
+  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const bool valid = c < nchunk;
+    float e0, e1, e2, e3;
+    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    if (valid) {
+      const int q0 = clamp_i((int)rintf(e0 / s), -127, 127);
+      const int q1 = clamp_i((int)rintf(e1 / s), -127, 127);
+      const int q2 = clamp_i((int)rintf(e2 / s), -127, 127);
+      const int q3 = clamp_i((int)rintf(e3 / s), -127, 127);
+      *reinterpret_cast<u32*>(out + 4 * c) = (u32)(q0 & 0xFF) | ((u32)(q1 & 0xFF) << 8) |
+                                             ((u32)(q2 & 0xFF) << 16) | ((u32)(q3 & 0xFF) << 24);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int8_t* xq,
+                                    float* x_scale, hipStream_t stream) {
+  hipLaunchKernelGGL(k_act_rht_quant, dim3(M), dim3(kThreads), 0, stream, X, K, signs, xq, x_scale);
+  return hipGetLastError();
+}
+
+hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* signs, int group,
+                                   bool z4, uint8_t* wq, uint16_t* w_scale, void* w_zero,
+                                   float* w_rot, hipStream_t stream) {
+  const dim3 grid(N), block(kThreads);
+#define SVG_W4_CASE(G)                                                                            \
+  if (group == G) {                                                                               \
+    if (z4)                                                                                       \
+      hipLaunchKernelGGL((k_rot_quant_w4<G, true>), grid, block, 0, stream, W, K, signs, wq,      \
+                         w_scale, w_zero, w_rot);                                                 \
+    else                                                                                          \
+      hipLaunchKernelGGL((k_rot_quant_w4<G, false>), grid, block, 0, stream, W, K, signs, wq,     \
+                         w_scale, w_zero, w_rot);                                                 \
+    return hipGetLastError();                                                                     \
+  }
+  SVG_W4_CASE(32)
+  SVG_W4_CASE(64)
+  SVG_W4_CASE(128)
+#undef SVG_W4_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* signs, int8_t* wq,
+                                   uint16_t* w_scale, float* w_rot, hipStream_t stream) {
+  hipLaunchKernelGGL(k_rot_quant_w8, dim3(N), dim3(kThreads), 0, stream, W, K, signs, wq, w_scale,
+                     w_rot);
+  return hipGetLastError();
+}

@@ -1,0 +1,98 @@
+// Device helpers shared by the gfx950 kernels: cross-lane exchanges for the
+// 32-wide Walsh-Hadamard butterfly, nibble unpacking, int8 dot products and
+// loads.  Wave64 throughout.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#define SVG_DEV __device__ __forceinline__
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef unsigned u32;
+
+// ------------------------------------------------------- lane exchanges
+// xor-1 and xor-2 within a quad: DPP quad_perm; xor-4/8/16 within 32 lanes:
+// ds_swizzle in bit-mask mode (and=0x1f, xor=mask); xor-32: ds_bpermute.
+SVG_DEV int lane_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true); }
+SVG_DEV int lane_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true); }
+SVG_DEV int lane_xor4(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10)); }
+SVG_DEV int lane_xor8(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x1F | (8 << 10)); }
+SVG_DEV int lane_xor16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x1F | (16 << 10)); }
+SVG_DEV int lane_xor32(int v) {
+  const int lane = __lane_id();
+  return __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, v);
+}
+
+template <int MASK>
+SVG_DEV int lane_xor(int v) {
+  if constexpr (MASK == 1) return lane_xor1(v);
+  else if constexpr (MASK == 2) return lane_xor2(v);
+  else if constexpr (MASK == 4) return lane_xor4(v);
+  else if constexpr (MASK == 8) return lane_xor8(v);
+  else if constexpr (MASK == 16) return lane_xor16(v);
+  else return lane_xor32(v);
+}
+template <int MASK>
+SVG_DEV float lane_xorf(float v) { return __int_as_float(lane_xor<MASK>(__float_as_int(v))); }
+
+// ------------------------------------------- 32-wide Walsh-Hadamard butterfly
+// A block of 32 values is spread over 8 consecutive lanes, 4 consecutive
+// values per lane (lane j of the block holds elements 4j..4j+3).  Stages run
+// h = 1, 2 inside the lane, then h = 4, 8, 16 across lanes j^1, j^2, j^4.  At
+// every stage the lower element of a pair becomes (a + b) and the upper one
+// (a - b): one rounded fp32 operation each, in ascending stage order.
+#pragma clang fp contract(off)
+SVG_DEV void fwht32_lane4(float& e0, float& e1, float& e2, float& e3) {
+  const int j = __lane_id() & 7;
+  float a0 = e0 + e1, a1 = e0 - e1, a2 = e2 + e3, a3 = e2 - e3;  // h = 1
+  e0 = a0 + a2; e2 = a0 - a2; e1 = a1 + a3; e3 = a1 - a3;        // h = 2
+  {
+    float p0 = lane_xorf<1>(e0), p1 = lane_xorf<1>(e1), p2 = lane_xorf<1>(e2), p3 = lane_xorf<1>(e3);
+    const bool up = j & 1;                                         // h = 4
+    e0 = up ? p0 - e0 : e0 + p0; e1 = up ? p1 - e1 : e1 + p1;
+    e2 = up ? p2 - e2 : e2 + p2; e3 = up ? p3 - e3 : e3 + p3;
+  }
+  {
+    float p0 = lane_xorf<2>(e0), p1 = lane_xorf<2>(e1), p2 = lane_xorf<2>(e2), p3 = lane_xorf<2>(e3);
+    const bool up = j & 2;                                         // h = 8
+    e0 = up ? p0 - e0 : e0 + p0; e1 = up ? p1 - e1 : e1 + p1;
+    e2 = up ? p2 - e2 : e2 + p2; e3 = up ? p3 - e3 : e3 + p3;
+  }
+  {
+    float p0 = lane_xorf<4>(e0), p1 = lane_xorf<4>(e1), p2 = lane_xorf<4>(e2), p3 = lane_xorf<4>(e3);
+    const bool up = j & 4;                                         // h = 16
+    e0 = up ? p0 - e0 : e0 + p0; e1 = up ? p1 - e1 : e1 + p1;
+    e2 = up ? p2 - e2 : e2 + p2; e3 = up ? p3 - e3 : e3 + p3;
+  }
+}
+
+// Sign flip of four values by four packed int8 signs (+1 / -1): exact.
+SVG_DEV void apply_signs4(float& e0, float& e1, float& e2, float& e3, int packed) {
+  e0 = e0 * (float)(int8_t)(packed & 0xFF);
+  e1 = e1 * (float)(int8_t)((packed >> 8) & 0xFF);
+  e2 = e2 * (float)(int8_t)((packed >> 16) & 0xFF);
+  e3 = e3 * (float)(int8_t)((packed >> 24) & 0xFF);
+}
+
+// --------------------------------------------------------------- integers
+// Packed word of 8 nibbles (k = 0..7, nibble i at bits 4i) -> two int8x4
+// words: even-k codes {0,2,4,6} and odd-k codes {1,3,5,7}.
+SVG_DEV u32 nib_even(u32 w) { return w & 0x0F0F0F0Fu; }
+SVG_DEV u32 nib_odd(u32 w) { return (w >> 4) & 0x0F0F0F0Fu; }
+// The matching reorder of 8 int8 activation codes held in two words
+// (a0 = k 0..3, a1 = k 4..7): even-k bytes and odd-k bytes.
+SVG_DEV u32 act_even(u32 a0, u32 a1) { return __builtin_amdgcn_perm(a1, a0, 0x06040200u); }
+SVG_DEV u32 act_odd(u32 a0, u32 a1) { return __builtin_amdgcn_perm(a1, a0, 0x07050301u); }
+
+SVG_DEV int dot4(u32 a, u32 b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
+
+// ------------------------------------------------------------------ loads
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+SVG_DEV uint4 load_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+SVG_DEV uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+SVG_DEV float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }

@@ -1,0 +1,134 @@
+// C ABI entry points (include/svgemm.h): host-side validation, then one
+// enqueue on the caller's stream.  No allocation, no synchronisation, no state
+// shared between calls apart from the per-thread error text.
+#include "../../include/svgemm.h"
+
+#include <stdint.h>
+
+#include <cstdio>
+#include <string>
+
+#include "svg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+svg_status fail(svg_status code, const char* fn, const char* what) {
+  g_last_error = std::string(fn) + ": " + what;
+  return code;
+}
+
+svg_status ok() {
+  g_last_error.clear();
+  return SVG_OK;
+}
+
+svg_status hip_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return ok();
+  g_last_error = std::string(fn) + ": HIP error " + std::to_string((int)e) + " (" +
+                 hipGetErrorName(e) + "): " + hipGetErrorString(e);
+  return SVG_EHIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+
+constexpr int kMaxM = 32;
+constexpr int kMaxKW8 = 131072;  // 127^2 * K < 2^31
+
+}  // namespace
+
+extern "C" {
+
+const char* svg_last_error(void) { return g_last_error.c_str(); }
+
+svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs, int block, int fmt,
+                              int group, void* wq, uint16_t* w_scale, void* w_zero,
+                              float* w_rot_debug, void* stream) {
+  static const char* fn = "rht_rotate_weights";
+  if (N < 0) return fail(SVG_EINVAL, fn, "N < 0");
+  if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
+  if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16 && fmt != SVG_W8_SYM)
+    return fail(SVG_EUNSUPPORTED, fn, "unknown fmt");
+  if (block != 32) return fail(SVG_EUNSUPPORTED, fn, "block must be 32");
+  if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  const bool w4 = fmt != SVG_W8_SYM;
+  if (w4 && !group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
+  if (w4 && K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of group");
+  if (!W || !signs || !wq || !w_scale || (w4 && !w_zero))
+    return fail(SVG_EINVAL, fn, "null required pointer");
+  if (!aligned(W, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "W and wq need 16-byte alignment");
+  if (!aligned(signs, 4)) return fail(SVG_EALIGN, fn, "signs needs 4-byte alignment");
+  if (!aligned(w_scale, 2) || (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 2)))
+    return fail(SVG_EALIGN, fn, "w_scale / fp16 w_zero need 2-byte alignment");
+  if (w_rot_debug && !aligned(w_rot_debug, 16)) return fail(SVG_EALIGN, fn, "w_rot_debug needs 16-byte alignment");
+  if (N == 0) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (w4)
+    e = svg_launch_rot_quant_w4(W, N, K, signs, group, fmt == SVG_W4_ASYM_Z4,
+                                reinterpret_cast<uint8_t*>(wq), w_scale, w_zero, w_rot_debug, s);
+  else
+    e = svg_launch_rot_quant_w8(W, N, K, signs, reinterpret_cast<int8_t*>(wq), w_scale, w_rot_debug, s);
+  return hip_status(fn, e);
+}
+
+svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs, int block,
+                            int8_t* xq, float* x_scale, void* stream) {
+  static const char* fn = "act_rht_quant_i8";
+  if (M < 0) return fail(SVG_EINVAL, fn, "M < 0");
+  if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
+  if (block != 32) return fail(SVG_EUNSUPPORTED, fn, "block must be 32");
+  if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
+  if (!X || !signs || !xq || !x_scale) return fail(SVG_EINVAL, fn, "null required pointer");
+  if (!aligned(X, 16) || !aligned(xq, 16)) return fail(SVG_EALIGN, fn, "X and xq need 16-byte alignment");
+  if (!aligned(signs, 4) || !aligned(x_scale, 4)) return fail(SVG_EALIGN, fn, "signs / x_scale need 4-byte alignment");
+  if (M == 0) return ok();
+  return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, xq, x_scale,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
+                       const uint16_t* w_scale, const void* w_zero, int fmt, int group, int N,
+                       float* y, int32_t* partials_debug, void* stream) {
+  static const char* fn = "w4a8_linear";
+  if (M < 0 || N < 0) return fail(SVG_EINVAL, fn, "M < 0 or N < 0");
+  if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
+  if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16) return fail(SVG_EUNSUPPORTED, fn, "fmt must be a W4 format");
+  if (!group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
+  if (K % 32 || K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32 and of group");
+  if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
+  if (!xq || !x_scale || !wq || !w_scale || !w_zero || !y) return fail(SVG_EINVAL, fn, "null required pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "xq and wq need 16-byte alignment");
+  if (!aligned(x_scale, 4) || !aligned(y, 4) || !aligned(w_scale, 2) ||
+      (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 2)) || (partials_debug && !aligned(partials_debug, 4)))
+    return fail(SVG_EALIGN, fn, "misaligned scale, zero, y or partials pointer");
+  if (M == 0 || N == 0) return ok();
+  return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
+                                        group, N, y, partials_debug,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
+                       const uint16_t* w_scale, int N, float* y, int32_t* partials_debug,
+                       void* stream) {
+  static const char* fn = "w8a8_linear";
+  if (M < 0 || N < 0) return fail(SVG_EINVAL, fn, "M < 0 or N < 0");
+  if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
+  if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  if (K > kMaxKW8) return fail(SVG_EUNSUPPORTED, fn, "K > 131072 would overflow int32 partial sums");
+  if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
+  if (!xq || !x_scale || !wq || !w_scale || !y) return fail(SVG_EINVAL, fn, "null required pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "xq and wq need 16-byte alignment");
+  if (!aligned(x_scale, 4) || !aligned(y, 4) || !aligned(w_scale, 2) ||
+      (partials_debug && !aligned(partials_debug, 4)))
+    return fail(SVG_EALIGN, fn, "misaligned scale, y or partials pointer");
+  if (M == 0 || N == 0) return ok();
+  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+"""Shared GPU-test plumbing: move seeded inputs to the device, run the library
+entry points through the binding, and fetch results.  No arithmetic of the
+method lives here: the expected values come from oracle/ only."""
+import sys
+
+import numpy as np
+import torch
+
+import speculative_verify_gemm_amd as svg
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def gpu_quant_acts(x, signs):
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    xs = torch.empty((M,), dtype=torch.float32, device=DEV)
+    svg.act_rht_quant_i8(to_dev(x), to_dev(signs), xq, xs)
+    return xq, xs
+
+
+def gpu_prepare(W, signs, fmt, group, debug=False):
+    """W: numpy [N,K] fp32 or a device tensor."""
+    Wd = W if isinstance(W, torch.Tensor) else to_dev(W)
+    N, K = Wd.shape
+    wq, ws, wz = svg.empty_weights(N, K, fmt, group)
+    rot = torch.empty((N, K), dtype=torch.float32, device=DEV) if debug else None
+    svg.rht_rotate_weights(Wd, to_dev(signs), fmt, group, wq, ws, wz, rot)
+    return dict(wq=wq, ws=ws, wz=wz, rot=rot, fmt=fmt, group=group, N=N, K=K)
+
+
+def gpu_linear(xq, xs, w, debug=True):
+    M, K = xq.shape
+    N = w["N"]
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    if w["fmt"] == "w8":
+        dbg = torch.empty((M, N), dtype=torch.int32, device=DEV) if debug else None
+        svg.w8a8_linear(xq, xs, w["wq"], w["ws"], y, dbg)
+    else:
+        dbg = torch.empty((M, N, K // w["group"]), dtype=torch.int32, device=DEV) if debug else None
+        svg.w4a8_linear(xq, xs, w["wq"], w["ws"], w["wz"], w["fmt"], w["group"], y, dbg)
+    return y, dbg
+
+
+def oracle_weights_to_dev(ow, fmt):
+    """Device copies of the oracle's encoded weights, in the library layout."""
+    from oracle import svg_oracle as O
+    if fmt == "w8":
+        return dict(wq=to_dev(ow["q"]), ws=to_dev(ow["s"]), wz=None, fmt=fmt, group=0,
+                    N=ow["q"].shape[0], K=ow["q"].shape[1])
+    z = O.pack_z4(ow["z"]) if fmt == "w4_z4" else O.zeros_as_f16(ow["z"])
+    return dict(wq=to_dev(O.pack_w4_codes(ow["q"])), ws=to_dev(ow["s"]), wz=to_dev(z), fmt=fmt,
+                group=ow["group"], N=ow["q"].shape[0], K=ow["q"].shape[1])
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f16_bits(a):
+    return np.asarray(a).view(np.uint16) if np.asarray(a).dtype == np.float16 else np.asarray(a)

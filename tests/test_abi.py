@@ -1,0 +1,114 @@
+"""The C ABI library loads, exports every entry point the header declares, and
+rejects bad arguments on the host with the documented status codes.
+
+No GPU: every call here fails validation (or is an empty call) before
+anything could be enqueued, so no pointer passed is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svgemm.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M))
+                  - {"if", "defined"})
+
+
+@pytest.fixture(scope="module")
+def svg():
+    import speculative_verify_gemm_amd as svg
+    return svg
+
+
+def test_header_declares_the_entry_points():
+    assert _header_functions() == sorted(
+        ["act_rht_quant_i8", "rht_rotate_weights", "svg_last_error", "w4a8_linear", "w8a8_linear"])
+
+
+def test_library_exports_every_declared_symbol(svg):
+    for name in _header_functions():
+        assert hasattr(svg.lib, name), name
+        assert ctypes.cast(getattr(svg.lib, name), ctypes.c_void_p).value
+
+
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10001)    # misaligned
+NULL = None
+
+
+def _w4(svg, **kw):
+    args = dict(xq=A, xs=A, M=1, K=128, wq=A, ws=A, wz=A, fmt=1, g=64, N=16, y=A, dbg=NULL)
+    args.update(kw)
+    return svg.lib.w4a8_linear(args["xq"], args["xs"], args["M"], args["K"], args["wq"], args["ws"],
+                               args["wz"], args["fmt"], args["g"], args["N"], args["y"], args["dbg"],
+                               NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(xq=NULL), 1), (dict(y=NULL), 1), (dict(wz=NULL), 1), (dict(M=-1), 1), (dict(K=0), 1),
+    (dict(N=-3), 1),
+    (dict(g=16), 2), (dict(g=96), 2), (dict(K=96, g=64), 2), (dict(K=48, g=32), 2),
+    (dict(M=33), 2), (dict(fmt=2), 2), (dict(fmt=7), 2),
+    (dict(xq=MIS), 3), (dict(wq=MIS), 3), (dict(y=MIS), 3), (dict(ws=MIS), 3),
+])
+def test_w4a8_validation(svg, kw, code):
+    assert _w4(svg, **kw) == code
+    assert svg.last_error().startswith("w4a8_linear:")
+
+
+def test_empty_calls_are_ok(svg):
+    assert _w4(svg, M=0) == 0 and svg.last_error() == ""
+    assert _w4(svg, N=0) == 0
+    assert svg.lib.act_rht_quant_i8(A, 0, 64, A, 32, A, A, NULL) == 0
+    assert svg.lib.rht_rotate_weights(A, 0, 64, A, 32, 1, 32, A, A, A, NULL, NULL) == 0
+    assert svg.lib.w8a8_linear(A, A, 0, 64, A, A, 8, A, NULL, NULL) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, 1, 64, A, 32, A, A), 1), ((A, -1, 64, A, 32, A, A), 1), ((A, 1, 0, A, 32, A, A), 1),
+    ((A, 1, 64, A, 16, A, A), 2), ((A, 1, 48, A, 32, A, A), 2), ((A, 33, 64, A, 32, A, A), 2),
+    ((MIS, 1, 64, A, 32, A, A), 3), ((A, 1, 64, MIS, 32, A, A), 3), ((A, 1, 64, A, 32, MIS, A), 3),
+])
+def test_act_quant_validation(svg, args, code):
+    assert svg.lib.act_rht_quant_i8(*args, NULL) == code
+    assert svg.last_error().startswith("act_rht_quant_i8:")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, 4, 64, A, 32, 1, 32, A, A, A, NULL), 1),
+    ((A, 4, 64, A, 32, 0, 32, A, A, NULL, NULL), 1),     # W4 needs w_zero
+    ((A, 4, 64, A, 32, 3, 32, A, A, A, NULL), 2),        # unknown fmt
+    ((A, 4, 64, A, 64, 1, 32, A, A, A, NULL), 2),        # block != 32
+    ((A, 4, 96, A, 32, 1, 64, A, A, A, NULL), 2),        # K % group
+    ((A, 4, 64, A, 32, 1, 48, A, A, A, NULL), 2),        # group
+    ((A, 4, 64, MIS, 32, 1, 32, A, A, A, NULL), 3),      # signs alignment
+    ((A, 4, 64, A, 32, 2, 0, MIS, A, NULL, NULL), 3),    # wq alignment
+])
+def test_rotate_validation(svg, args, code):
+    assert svg.lib.rht_rotate_weights(*args, NULL) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A, A, 1, 64, A, A, 8, NULL, NULL), 1),
+    ((A, A, 1, 131104, A, A, 8, A, NULL), 2),
+    ((A, A, 1, 48, A, A, 8, A, NULL), 2),
+    ((A, A, 40, 64, A, A, 8, A, NULL), 2),
+    ((A, A, 1, 64, MIS, A, 8, A, NULL), 3),
+])
+def test_w8a8_validation(svg, args, code):
+    assert svg.lib.w8a8_linear(*args, NULL) == code
+
+
+def test_binding_has_no_cpu_path(svg):
+    import torch
+    x = torch.zeros((1, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        svg.act_rht_quant_i8(x, torch.ones(64, dtype=torch.int8), torch.zeros((1, 64), dtype=torch.int8),
+                             torch.zeros(1))
