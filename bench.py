@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the RHT + W4A8 / W8A8 quantized linear on one MI355X.
+
+A step is one pass over a ~7B-parameter synthetic projection stack (32 layers
+of q/k/v/o 4096x4096, gate/up 4096->12288, down 12288->4096): for each layer
+and each of its four input spaces, the activation rows are rotated and
+quantized (act_rht_quant_i8), then the linear(s) consuming them run (q/k/v
+stacked along N into one launch, gate/up into one).  Weights are rotated and
+quantized once at setup (rht_rotate_weights) and stay resident in HBM.  The
+pass is captured in a HIP graph and replayed.
+
+Printed: ONE JSON line.  `value` is algorithmic bytes per pass (packed weights,
+scales and zeros, int8 activations in, fp32 outputs out) / wall time per pass,
+in GB/s.  `roofline` reports the dominant kernel (the linear) timed per launch
+with HIP events on its stream; `cpu_baseline` times the CPU oracle on one
+layer of the same workload.
+
+The pages behind the method ("Karpathy's Trick for Faster Local LLMs Finally
+Has Proper Tooling", blog.dailydoseofds.com, section "Why batch-one decoding
+is memory-bound") bound decode speed by bandwidth / bytes per pass; the
+passes/s and tokens/s ceilings reported here follow that closed form.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_I8_TOPS = 5000.0
+
+WORKLOADS = {
+    "stack_w4g64": dict(fmt="w4_z16", group=64, M=16,
+                        desc="32-layer ~7B projection stack, W4 asymmetric g64 (fp16 scale + fp16 zero), "
+                             "RHT block 32, int8 per-token activations, M=16 verify pass"),
+    "stack_w8": dict(fmt="w8", group=0, M=32,
+                     desc="32-layer ~7B projection stack, W8 symmetric per-channel fp16 scale, "
+                          "RHT block 32, int8 per-token activations, M=32 verify pass"),
+    "stack_w4g128": dict(fmt="w4_z16", group=128, M=32,
+                         desc="32-layer ~7B projection stack, W4 asymmetric g128 (fp16 scale + fp16 zero), "
+                              "RHT block 32 != group, heavy-tailed activations with 1% channels x100"),
+}
+
+# launches of one layer: (name, member matrices, N, K, input space)
+LAYER_LAUNCHES = (
+    ("qkv", ("q", "k", "v"), 12288, 4096, "attn_in"),
+    ("o", ("o",), 4096, 4096, "attn_out"),
+    ("gateup", ("gate", "up"), 24576, 4096, "mlp_in"),
+    ("down", ("down",), 4096, 12288, "mlp_mid"),
+)
+
+
+def linear_bytes(M, N, K, fmt, group):
+    """Algorithmic bytes of one linear launch: codes, scales, zeros, int8
+    activations and their scales in, fp32 outputs out."""
+    if fmt == "w8":
+        w = N * K + 2 * N
+    else:
+        G = K // group
+        z = N * ((G + 1) // 2) if fmt == "w4_z4" else 2 * N * G
+        w = N * K // 2 + 2 * N * G + z
+    return w + M * K + 4 * M + 4 * M * N
+
+
+def weight_bytes(N, K, fmt, group):
+    return linear_bytes(0, N, K, fmt, group)
+
+
+class Stack:
+    """The synthetic stack resident on the device, and its captured passes."""
+
+    def __init__(self, workload, layers, dev):
+        import torch
+        import speculative_verify_gemm_amd as svg
+        import synth
+        self.torch, self.svg, self.synth = torch, svg, synth
+        self.wl = workload
+        self.spec = WORKLOADS[workload]
+        self.fmt, self.group = self.spec["fmt"], self.spec["group"]
+        self.layers = layers
+        self.dev = dev
+        self.w = []       # per layer: {launch: (wq, ws, wz)}
+        self.signs = []   # per layer: {space: int8 device tensor}
+        t0 = time.time()
+        for L in range(layers):
+            signs = {sp: torch.from_numpy(synth.stack_signs(L, sp)).to(dev) for sp, _k in synth.STACK_SPACES}
+            lw = {}
+            for name, members, N, K, space in LAYER_LAUNCHES:
+                wq, ws, wz = svg.empty_weights(N, K, self.fmt, self.group, device=dev)
+                r0 = 0
+                for mname in members:
+                    W = synth.stack_weight(L, mname, device=dev)
+                    n = W.shape[0]
+                    mq, ms, mz = svg.stacked_slices(wq, ws, wz, r0, n, K, self.fmt, self.group)
+                    svg.rht_rotate_weights(W, signs[space], self.fmt, self.group, mq, ms, mz)
+                    r0 += n
+                    del W
+                lw[name] = (wq, ws, wz, N)
+            self.w.append(lw)
+            self.signs.append(signs)
+        torch.cuda.synchronize(dev)
+        self.setup_s = time.time() - t0
+
+    def make_inputs(self, M):
+        """fp32 activations per (layer, space) and the per-pass buffers."""
+        torch, synth = self.torch, self.synth
+        xin, xq, xs, ys = [], [], [], []
+        for L in range(self.layers):
+            d = {}
+            for sp, K in synth.STACK_SPACES:
+                d[sp] = torch.from_numpy(synth.stack_acts(self.wl, L, sp, M)).to(self.dev)
+            xin.append(d)
+            ys.append({name: torch.empty((M, N), dtype=torch.float32, device=self.dev)
+                       for name, _m, N, _k, _s in LAYER_LAUNCHES})
+        for sp, K in synth.STACK_SPACES:
+            xq.append(torch.empty((M, K), dtype=torch.int8, device=self.dev))
+            xs.append(torch.empty((M,), dtype=torch.float32, device=self.dev))
+        return dict(M=M, xin=xin, xq=dict(zip([s for s, _ in synth.STACK_SPACES], xq)),
+                    xs=dict(zip([s for s, _ in synth.STACK_SPACES], xs)), ys=ys)
+
+    def linear(self, io, L, name, space):
+        wq, ws, wz, N = self.w[L][name]
+        if self.fmt == "w8":
+            self.svg.w8a8_linear(io["xq"][space], io["xs"][space], wq, ws, N, io["ys"][L][name])
+        else:
+            self.svg.w4a8_linear(io["xq"][space], io["xs"][space], wq, ws, wz, self.fmt, self.group,
+                                 N, io["ys"][L][name])
+
+    def run_pass(self, io, events=None):
+        svg = self.svg
+        for L in range(self.layers):
+            for name, _members, _N, _K, space in LAYER_LAUNCHES:
+                svg.act_rht_quant_i8(io["xin"][L][space], self.signs[L][space], io["xq"][space], io["xs"][space])
+                if events is not None:
+                    e0, e1 = events.pop()
+                    e0.record()
+                    self.linear(io, L, name, space)
+                    e1.record()
+                else:
+                    self.linear(io, L, name, space)
+
+    def pass_bytes(self, M):
+        return sum(linear_bytes(M, N, K, self.fmt, self.group) for _n, _m, N, K, _s in LAYER_LAUNCHES) * self.layers
+
+    def capture(self, io):
+        torch = self.torch
+        s = torch.cuda.Stream(self.dev)
+        s.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(s):
+            self.run_pass(io)  # warm the launch path outside capture
+        torch.cuda.current_stream(self.dev).wait_stream(s)
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_pass(io)
+        torch.cuda.synchronize(self.dev)
+        return g
+
+
+def time_graph(torch, g, steps, warmup, dev):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / steps  # ms per pass
+
+
+def time_linear_launches(stack, io, steps):
+    """Per-launch duration of the linear kernel, from HIP events recorded on
+    the stream it is launched on (eager passes)."""
+    torch = stack.torch
+    per_pass = stack.layers * len(LAYER_LAUNCHES)
+    durs = []
+    bytes_per_launch = [linear_bytes(io["M"], N, K, stack.fmt, stack.group)
+                        for _L in range(stack.layers) for _n, _m, N, K, _s in LAYER_LAUNCHES]
+    for _ in range(steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(per_pass)]
+        order = list(evs)
+        stack.run_pass(io, events=list(reversed(evs)))
+        torch.cuda.synchronize(stack.dev)
+        durs.extend(a.elapsed_time(b) for a, b in order)
+    mean_ms = sum(durs) / len(durs)
+    mean_bytes = sum(bytes_per_launch) / len(bytes_per_launch)
+    return mean_ms, mean_bytes, len(durs)
+
+
+def kernel_name(fmt, group, M):
+    if M <= 2:
+        return "k_w8a8_dot" if fmt == "w8" else "k_w4a8_dot"
+    return "k_w8a8_mfma" if fmt == "w8" else "k_w4a8_mfma"
+
+
+def cpu_baseline(stack, M):
+    """The CPU oracle on layer 0 of the same workload (the four launches of
+    one layer, all rows): weights copied from the device generator and encoded
+    by the oracle (untimed), then the per-pass steps (activation rotation and
+    quantization, integer contraction, fp64 output) timed."""
+    import numpy as np
+    synth = stack.synth
+    from oracle import svg_oracle as O
+    L = 0
+    prepared = []
+    for name, members, N, K, space in LAYER_LAUNCHES:
+        Ws = [synth.stack_weight(L, m, device=stack.dev).cpu().numpy() for m in members]
+        W = np.concatenate(Ws, axis=0)
+        signs = synth.stack_signs(L, space)
+        ow = O.prepare_w8(W, signs) if stack.fmt == "w8" else O.prepare_w4(W, signs, stack.group)
+        x = synth.stack_acts(stack.wl, L, space, M)
+        prepared.append((x, signs, ow, N, K))
+        del W, Ws
+    t0 = time.perf_counter()
+    for x, signs, ow, N, K in prepared:
+        if stack.fmt == "w8":
+            O.linear_w8(x, signs, ow)
+        else:
+            O.linear_w4(x, signs, ow)
+    dt = time.perf_counter() - t0
+    nbytes = sum(linear_bytes(M, N, K, stack.fmt, stack.group) for _x, _s, _o, N, K in prepared)
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"layer 0 of the same stack (qkv, o, gate/up, down; {nbytes / 1e6:.1f} MB of "
+                       f"algorithmic bytes) at M={M}: activation RHT + int8 quantization, exact "
+                       f"integer contraction, fp64 output; numpy, single thread; {dt:.2f} s",
+                seconds=dt, cpu=platform.processor() or platform.machine())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stack_w4g64", choices=sorted(WORKLOADS))
+    ap.add_argument("--m", type=int, default=None, help="tokens per pass (default: the workload's)")
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the M=1 comparison pass")
+    ap.add_argument("--sweep", default=None, help="comma-separated M values: report a pass per M")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the linear shards by output rows with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    spec = WORKLOADS[args.workload]
+    M = args.m or spec["M"]
+    print(f"[bench] building {args.workload} ({args.layers} layers) on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    stack = Stack(args.workload, args.layers, dev)
+    print(f"[bench] weights resident after {stack.setup_s:.1f} s", file=sys.stderr, flush=True)
+
+    def measure(m):
+        io = stack.make_inputs(m)
+        g = stack.capture(io)
+        ms = time_graph(torch, g, args.steps, args.warmup, dev)
+        nbytes = stack.pass_bytes(m)
+        print(f"[bench] M={m}: {ms:.4f} ms/pass, {nbytes / ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
+        return io, g, ms, nbytes
+
+    io, g, ms, nbytes = measure(M)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    kmean_ms, kbytes, nlaunch = time_linear_launches(stack, io, max(1, min(args.steps, 5)))
+    k_gbps = kbytes / (kmean_ms * 1e-3) / 1e9
+    ops_per_pass = sum(2 * M * N * K for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
+    wbytes = sum(weight_bytes(N, K, stack.fmt, stack.group) for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
+    out = {
+        "metric": "W4A8 linear: achieved HBM GB/s and % of peak at M=1 and M=16 (verify)",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if stack.fmt == "w8" else "int8xint4",
+        "data": "synthetic (seeded; weights drawn on the device, activations on the host)",
+        "config": {"workload": args.workload, "description": spec["desc"], "M": M,
+                   "layers": args.layers, "weight_format": stack.fmt, "group": stack.group,
+                   "bytes_per_pass": nbytes, "weight_bytes_per_pass": wbytes,
+                   "launches_per_pass": args.layers * len(LAYER_LAUNCHES) * 2},
+        "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "passes_per_s": round(1e3 / ms, 2),
+        "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1)},
+        "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M),
+                     "achieved": round(k_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(k_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "mean_launch_us": round(kmean_ms * 1e3, 3),
+                     "mean_algorithmic_bytes_per_launch": round(kbytes),
+                     "launches_timed": nlaunch,
+                     "int8_tops": round(ops_per_pass / (ms * 1e-3) / 1e12, 2)},
+    }
+    if args.workload != "stack_w8" and M != 1 and not args.no_decode:
+        del g
+        _io1, g1, ms1, nbytes1 = measure(1)
+        out["decode_m1"] = {"ms_per_pass": round(ms1, 5), "GB_per_s": round(nbytes1 / (ms1 * 1e-3) / 1e9, 2),
+                            "frac_of_hbm_peak": round(nbytes1 / (ms1 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                            "bytes_per_pass": nbytes1}
+        out[f"verify_m{M}_over_decode_m1"] = round(ms / ms1, 4)
+        del g1
+    if args.sweep:
+        rows = []
+        for m in [int(v) for v in args.sweep.split(",")]:
+            _iom, gm, msm, nbm = measure(m)
+            rows.append({"M": m, "ms_per_pass": round(msm, 5), "GB_per_s": round(nbm / (msm * 1e-3) / 1e9, 2),
+                         "bytes_per_pass": nbm})
+            del gm
+        out["sweep"] = rows
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
+        cb = cpu_baseline(stack, M)
+        out["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,12 +54,41 @@ enum {
 };
 
 enum {
-    SVG_W4_ASYM_Z4 = 0,   /* codes u8 [N][K/2]; scale fp16 [N][K/g];
-                             zero u4 packed two per byte [N][(K/g + 1)/2]     */
-    SVG_W4_ASYM_Z16 = 1,  /* codes u8 [N][K/2]; scale fp16 [N][K/g];
-                             zero fp16 (integer 0..15) [N][K/g]               */
-    SVG_W8_SYM = 2        /* codes i8 [N][K]; scale fp16 [N]; no zero          */
+    SVG_W4_ASYM_Z4 = 0,   /* 4-bit asymmetric codes, fp16 scale, 4-bit zero      */
+    SVG_W4_ASYM_Z16 = 1,  /* 4-bit asymmetric codes, fp16 scale, fp16 zero       */
+    SVG_W8_SYM = 2        /* 8-bit symmetric codes, one fp16 scale per row       */
 };
+
+/*
+ * Weight storage ("tiled"; the pages give no layout -- this one lets a wave read
+ * each 16-row tile of a matrix as contiguous KiB in the lane order of the
+ * int8 MFMA, v_mfma_i32_16x16x64_i8).
+ *
+ * W4 codes (wq): rows padded to Np = ceil(N/16)*16 and K to Kp = ceil(K/128)*128
+ *   with code 0.  Tile (i, j) -- rows 16i..16i+15, k 128j..128j+127 -- is the
+ *   1024 bytes at (i*Kp/128 + j)*1024.  Its 16-byte piece p = 16b + r
+ *   (b = 0..3, r = 0..15) belongs to row 16i + r: bytes 0..7 hold
+ *   k in [128j+16b, +16), bytes 8..15 hold k in [128j+64+16b, +16).  A 4-byte
+ *   word covering k0..k0+7 holds code k0+t in the low nibble and code k0+t+4 in
+ *   the high nibble of byte t.  Size Np*Kp/2 bytes.
+ * W4 scales (fp16) and fp16 zeros: one value per (row, group); rows padded
+ *   to 16 and K to a multiple of 512 with 0.  The 512/group values of
+ *   (16-row tile i, 512-k block jb, row r) are contiguous, blocks ordered by
+ *   (i, jb, r): value (n, g) sits at ((i*KB + jb)*16 + r)*(512/group) + c with
+ *   i = n/16, r = n%16, jb = g/(512/group), c = g%(512/group), KB = ceil(K/512).
+ *   Size Np*KB*(512/group) values.
+ * W4 4-bit zeros: the same order, two per byte (even index in the low nibble).
+ * W8 codes: rows padded to 16 and K to Kp8 = ceil(K/64)*64 with 0; tile (i, j)
+ *   -- 16 rows x 64 k -- is 1024 bytes at (i*Kp8/64 + j)*1024; piece 16b + r
+ *   holds row 16i + r, k in [64j+16b, +16) in natural order.  W8 scales: fp16
+ *   [N] in row order.
+ *
+ * svg_weight_sizes gives the byte sizes a caller must allocate (host-only;
+ * touches no device).  SVG_EINVAL / SVG_EUNSUPPORTED as for
+ * rht_rotate_weights; zero_bytes is 0 for W8.
+ */
+svg_status svg_weight_sizes(int N, int K, int fmt, int group, uint64_t* wq_bytes,
+                            uint64_t* scale_bytes, uint64_t* zero_bytes);
 
 /*
  * rht_rotate_weights -- offline: rotate and quantize the rows of W.
@@ -75,12 +104,10 @@ enum {
  *  fmt      SVG_W4_ASYM_Z4, SVG_W4_ASYM_Z16 or SVG_W8_SYM.
  *  group    W4: quantization group along K, 32, 64 or 128 (independent of the
  *           transform block).  Ignored for W8.
- *  wq       W4: u8 [N][K/2], byte j of a row holds code k=2j in its low nibble
- *           and k=2j+1 in its high nibble; W8: i8 [N][K].  16-byte aligned.
- *  w_scale  fp16 bits; W4: [N][K/group]; W8: [N].  2-byte aligned.
- *  w_zero   W4 Z4: u8 [N][(K/group + 1)/2], group 2j in the low nibble;
- *           W4 Z16: fp16 bits [N][K/group], integer values 0..15;
- *           W8: unused, may be NULL.
+ *  wq, w_scale, w_zero  outputs in the tiled storage above, sized by
+ *           svg_weight_sizes; wq 16-byte aligned, w_scale and fp16 w_zero
+ *           4-byte aligned; w_zero unused (may be NULL) for W8.  Padding is
+ *           written as zeros.
  *  w_rot_debug  nullable fp32 [N][K]: receives the rotated rows u (tests).
  *
  *  Per row, u = H_32 . diag(signs) . W[n] blockwise (butterfly stages
@@ -88,6 +115,9 @@ enum {
  *  hi = max(0, max u), s = fp16(rne((hi - lo) / 15)) (1.0 if zero),
  *  z = rint(-lo / s), q = clamp(rint(u / s) + z, 0, 15).  W8 per row:
  *  s = fp16(rne(max|u| / 127)) (1.0 if zero), q = clamp(rint(u / s), -127, 127).
+ *  Matrices whose rows are stacked along N (e.g. the q, k and v projections)
+ *  may be rotated one at a time into consecutive 16-row tiles of one buffer
+ *  when each has a multiple of 16 rows.
  */
 svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
                               int block, int fmt, int group, void* wq,
@@ -120,8 +150,9 @@ svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs,
  *  decoding is memory-bound": each pass streams every weight once.]
  *
  *  xq, x_scale   from act_rht_quant_i8 (xq 16-byte aligned), M in 1..32.
- *  wq, w_scale, w_zero, fmt (SVG_W4_ASYM_Z4 or _Z16), group: from
- *                rht_rotate_weights with the same signs, N rows, K columns.
+ *  wq, w_scale, w_zero, fmt (SVG_W4_ASYM_Z4 or _Z16), group: the tiled
+ *                storage from rht_rotate_weights with the same signs, N rows,
+ *                K columns (wq 16-byte, w_scale and fp16 w_zero 4-byte aligned).
  *  y             fp32 [M][N], 4-byte aligned.
  *  partials_debug  nullable int32 [M][N][K/group]: receives
  *                S_g[m][n] = sum_{k in g} xq[m][k] * (q[n][k] - z[n][g]),
@@ -141,9 +172,9 @@ svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
  *  8-bit symmetric; both operands are integers.]
  *
  *  xq, x_scale   from act_rht_quant_i8 (xq 16-byte aligned), M in 1..32.
- *  wq            int8 [N][K] from rht_rotate_weights (SVG_W8_SYM), 16-byte
- *                aligned; w_scale fp16 bits [N].  K <= 131072 (so that
- *                |S| <= 127^2 K fits int32).
+ *  wq            tiled int8 codes from rht_rotate_weights (SVG_W8_SYM),
+ *                16-byte aligned; w_scale fp16 bits [N].  K <= 131072 (so
+ *                that |S| <= 127^2 K fits int32).
  *  y             fp32 [M][N].
  *  partials_debug  nullable int32 [M][N]: S[m][n] = sum_k xq[m][k] * q[n][k].
  *

@@ -43,6 +43,9 @@ def _load():
     lib.w8a8_linear.argtypes = [vp, vp, i, i, vp, vp, i, vp, vp, vp]
     for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear):
         fn.restype = ctypes.c_int
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.svg_weight_sizes.argtypes = [i, i, i, i, u64p, u64p, u64p]
+    lib.svg_weight_sizes.restype = ctypes.c_int
     lib.svg_last_error.argtypes = []
     lib.svg_last_error.restype = ctypes.c_char_p
     return lib
@@ -92,27 +95,37 @@ def _fmt(fmt):
 
 
 # ------------------------------------------------------------ entry points
+def weight_sizes(N, K, fmt, group):
+    """Bytes of the tiled weight storage: (wq, scales, zeros)."""
+    a, b, c = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib.svg_weight_sizes(N, K, _fmt(fmt), group, ctypes.byref(a), ctypes.byref(b),
+                                ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def _check_storage(N, K, f, group, wq, w_scale, w_zero):
+    wb, sb, zb = weight_sizes(N, K, f, group)
+    _dev(wq, "wq", torch.int8 if f == W8 else torch.uint8)
+    _dev(w_scale, "w_scale", torch.float16)
+    if wq.numel() < wb or w_scale.numel() * 2 < sb:
+        raise ValueError(f"weight storage too small: need {wb} code bytes and {sb} scale bytes")
+    if f != W8:
+        if w_zero is None:
+            raise ValueError("W4 formats need w_zero")
+        _dev(w_zero, "w_zero", torch.uint8 if f == W4_Z4 else torch.float16)
+        if w_zero.numel() * w_zero.element_size() < zb:
+            raise ValueError(f"w_zero too small: need {zb} bytes")
+
+
 def rht_rotate_weights(W, signs, fmt, group, wq, w_scale, w_zero=None, w_rot_debug=None,
                        block=BLOCK, stream=None):
-    """Rotate and quantize fp32 weights W[N, K] into (wq, w_scale, w_zero)."""
+    """Rotate and quantize fp32 weights W[N, K] into the tiled storage
+    (wq, w_scale, w_zero) sized by weight_sizes()."""
     f = _fmt(fmt)
     _dev(W, "W", torch.float32)
     _dev(signs, "signs", torch.int8)
     N, K = W.shape
-    if f == W8:
-        _dev(wq, "wq", torch.int8)
-        if tuple(wq.shape) != (N, K) or tuple(w_scale.shape) != (N,):
-            raise ValueError("W8 expects wq [N, K] and w_scale [N]")
-    else:
-        _dev(wq, "wq", torch.uint8)
-        G = K // group
-        zshape = (N, (G + 1) // 2) if f == W4_Z4 else (N, G)
-        if tuple(wq.shape) != (N, K // 2) or tuple(w_scale.shape) != (N, G) or \
-                w_zero is None or tuple(w_zero.shape) != zshape:
-            raise ValueError("W4 expects wq [N, K/2], w_scale [N, K/g], w_zero "
-                             f"{zshape}")
-        _dev(w_zero, "w_zero", torch.uint8 if f == W4_Z4 else torch.float16)
-    _dev(w_scale, "w_scale", torch.float16)
+    _check_storage(N, K, f, group, wq, w_scale, w_zero)
     if w_rot_debug is not None:
         _dev(w_rot_debug, "w_rot_debug", torch.float32)
     _check(lib.rht_rotate_weights(_p(W), N, K, _p(signs), block, f, group, _p(wq), _p(w_scale),
@@ -132,20 +145,17 @@ def act_rht_quant_i8(X, signs, xq, x_scale, block=BLOCK, stream=None):
                                 _stream(stream, X)))
 
 
-def w4a8_linear(xq, x_scale, wq, w_scale, w_zero, fmt, group, y, partials_debug=None,
+def w4a8_linear(xq, x_scale, wq, w_scale, w_zero, fmt, group, N, y, partials_debug=None,
                 stream=None):
-    """y[M, N] = dequantized (xq . W^T) for W4 weights."""
+    """y[M, N] = dequantized (xq . W^T) for tiled W4 weights of N rows."""
     f = _fmt(fmt)
     _dev(xq, "xq", torch.int8)
     _dev(x_scale, "x_scale", torch.float32)
-    _dev(wq, "wq", torch.uint8)
-    _dev(w_scale, "w_scale", torch.float16)
-    _dev(w_zero, "w_zero", torch.uint8 if f == W4_Z4 else torch.float16)
     _dev(y, "y", torch.float32)
     M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] * 2 != K or tuple(y.shape) != (M, N):
-        raise ValueError("shape mismatch between xq, wq and y")
+    _check_storage(N, K, f, group, wq, w_scale, w_zero)
+    if tuple(y.shape) != (M, N) or tuple(x_scale.shape) != (M,):
+        raise ValueError("y must be [M, N] and x_scale [M]")
     if partials_debug is not None:
         _dev(partials_debug, "partials_debug", torch.int32)
         if tuple(partials_debug.shape) != (M, N, K // group):
@@ -154,17 +164,15 @@ def w4a8_linear(xq, x_scale, wq, w_scale, w_zero, fmt, group, y, partials_debug=
                            N, _p(y), _p(partials_debug), _stream(stream, xq)))
 
 
-def w8a8_linear(xq, x_scale, wq, w_scale, y, partials_debug=None, stream=None):
-    """y[M, N] = dequantized (xq . W^T) for W8 weights."""
+def w8a8_linear(xq, x_scale, wq, w_scale, N, y, partials_debug=None, stream=None):
+    """y[M, N] = dequantized (xq . W^T) for tiled W8 weights of N rows."""
     _dev(xq, "xq", torch.int8)
     _dev(x_scale, "x_scale", torch.float32)
-    _dev(wq, "wq", torch.int8)
-    _dev(w_scale, "w_scale", torch.float16)
     _dev(y, "y", torch.float32)
     M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K or tuple(y.shape) != (M, N):
-        raise ValueError("shape mismatch between xq, wq and y")
+    _check_storage(N, K, W8, 0, wq, w_scale, None)
+    if tuple(y.shape) != (M, N) or tuple(x_scale.shape) != (M,):
+        raise ValueError("y must be [M, N] and x_scale [M]")
     if partials_debug is not None:
         _dev(partials_debug, "partials_debug", torch.int32)
         if tuple(partials_debug.shape) != (M, N):
@@ -175,16 +183,29 @@ def w8a8_linear(xq, x_scale, wq, w_scale, y, partials_debug=None, stream=None):
 
 # ------------------------------------------------------------- allocation
 def empty_weights(N, K, fmt, group, device="cuda"):
-    """Uninitialised output buffers for rht_rotate_weights: (wq, w_scale, w_zero)."""
+    """Uninitialised tiled storage for rht_rotate_weights: flat (wq, w_scale,
+    w_zero) tensors (w_zero is None for W8)."""
     f = _fmt(fmt)
+    wb, sb, zb = weight_sizes(N, K, f, group)
+    wq = torch.empty((wb,), dtype=torch.int8 if f == W8 else torch.uint8, device=device)
+    sc = torch.empty((sb // 2,), dtype=torch.float16, device=device)
     if f == W8:
-        return (torch.empty((N, K), dtype=torch.int8, device=device),
-                torch.empty((N,), dtype=torch.float16, device=device), None)
-    G = K // group
-    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=device)
-    sc = torch.empty((N, G), dtype=torch.float16, device=device)
+        return wq, sc, None
     if f == W4_Z4:
-        z = torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=device)
-    else:
-        z = torch.empty((N, G), dtype=torch.float16, device=device)
-    return wq, sc, z
+        return wq, sc, torch.empty((zb,), dtype=torch.uint8, device=device)
+    return wq, sc, torch.empty((zb // 2,), dtype=torch.float16, device=device)
+
+
+def stacked_slices(wq, w_scale, w_zero, rows_before, N, K, fmt, group):
+    """Views of the tiled storage of a matrix stacked after `rows_before` rows
+    (a multiple of 16) of other matrices in one buffer, N rows of its own."""
+    if rows_before % 16:
+        raise ValueError("stacked matrices must start on a 16-row tile")
+    f = _fmt(fmt)
+    w0, s0, z0 = weight_sizes(rows_before, K, f, group) if rows_before else (0, 0, 0)
+    w1, s1, z1 = weight_sizes(N, K, f, group)
+    if f == W8:
+        # W8 scales are per row, in row order
+        return wq[w0:w0 + w1], w_scale[rows_before:rows_before + N], None
+    es = w_zero.element_size()
+    return (wq[w0:w0 + w1], w_scale[s0 // 2:(s0 + s1) // 2], w_zero[z0 // es:(z0 + z1) // es])

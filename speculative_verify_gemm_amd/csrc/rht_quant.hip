@@ -103,6 +103,55 @@ __global__ __launch_bounds__(kThreads) void k_act_rht_quant(const float* __restr
   }
 }
 
+// Single-pass variant for K <= 4 * kThreads * CPT: every load of the row is
+// issued at once through buffer loads (zeros past K), the rotated values stay
+// in registers between the max reduction and the quantization.
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void k_act_rht_quant_reg(const float* __restrict__ X, int K,
+                                                               const int8_t* __restrict__ signs,
+                                                               int8_t* __restrict__ xq,
+                                                               float* __restrict__ x_scale) {
+  __shared__ float red[kThreads / 64];
+  const int m = blockIdx.x;
+  const int nchunk = K >> 2;
+  const rsrc_t xr = make_rsrc(X + (size_t)m * K, (u32)K * 4u);
+  const rsrc_t sr = make_rsrc(signs, (u32)K);
+  float e[CPT][4];
+  int sg[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const u32 c = threadIdx.x + kThreads * i;
+    const u32x4 v = bload16(xr, c * 16u);
+    sg[i] = (int)bload4(sr, c * 4u);
+    e[i][0] = __uint_as_float(v[0]); e[i][1] = __uint_as_float(v[1]);
+    e[i][2] = __uint_as_float(v[2]); e[i][3] = __uint_as_float(v[3]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    apply_signs4(e[i][0], e[i][1], e[i][2], e[i][3], sg[i]);
+    fwht32_lane4(e[i][0], e[i][1], e[i][2], e[i][3]);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e[i][0]), fabsf(e[i][1])), fmaxf(fabsf(e[i][2]), fabsf(e[i][3]))));
+  }
+  amax = block_max(amax, red);
+  const float sigma = amax / 127.0f;
+  if (threadIdx.x == 0) x_scale[m] = sigma * 0.03125f;  // exact: carries the transform's 2^-5
+  int8_t* out = xq + (size_t)m * K;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + kThreads * i;
+    if (c < nchunk) {
+      int q[4] = {0, 0, 0, 0};
+      if (amax > 0.f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) q[t] = clamp_i((int)rintf(e[i][t] / sigma), -127, 127);
+      }
+      *reinterpret_cast<u32*>(out + 4 * c) = (u32)(q[0] & 0xFF) | ((u32)(q[1] & 0xFF) << 8) |
+                                             ((u32)(q[2] & 0xFF) << 16) | ((u32)(q[3] & 0xFF) << 24);
+    }
+  }
+}
+
 // Group-wise min/max over the LPG = G/4 lanes that hold one quantization group.
 template <int LPG>
 SVG_DEV float group_min(float v) {
@@ -123,6 +172,24 @@ SVG_DEV float group_max(float v) {
   return v;
 }
 
+// Byte offset of the 4-byte word holding codes k0..k0+7 (k0 % 8 == 0) of row
+// n in the tiled W4 layout (see include/svgemm.h): tiles of 16 rows x 128 k,
+// 1 KiB each; piece 16*b + r of a tile holds row r's k-runs [16b, 16b+16) and
+// [64+16b, 64+16b+16) of the chunk.
+SVG_DEV size_t w4_word_offset(int n, int k0, int KT) {
+  const int i = n >> 4, r = n & 15;
+  const int j = k0 >> 7, kc = k0 & 127;
+  const int h = kc >> 6, b = (kc & 63) >> 4, w = (kc & 15) >> 3;
+  return ((size_t)i * KT + j) * 1024 + (size_t)(16 * b + r) * 16 + h * 8 + w * 4;
+}
+
+// Index of the (row n, group g) parameter in the blocked order: the
+// 512/group parameters of (16-row tile, 512-k block, row) are contiguous.
+SVG_DEV size_t w4_param_index(int n, int g, int KB, int gpb) {
+  const int i = n >> 4, r = n & 15, jb = g / gpb, c = g % gpb;
+  return (((size_t)i * KB + jb) * 16 + r) * gpb + c;
+}
+
 template <int G, bool Z4>
 __global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restrict__ W, int K,
                                                           const int8_t* __restrict__ signs,
@@ -130,11 +197,13 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restri
                                                           uint16_t* __restrict__ w_scale,
                                                           void* __restrict__ w_zero,
                                                           float* __restrict__ w_rot) {
-  constexpr int LPG = G / 4;  // lanes per group (8, 16 or 32)
+  constexpr int LPG = G / 4;            // lanes per group (8, 16 or 32)
+  constexpr int GPB = kMetaK / G;       // groups per 512-k parameter block
   const int n = blockIdx.x;
+  const int KB = (K + kMetaK - 1) / kMetaK;
   const float* row = W + (size_t)n * K;
   const int nchunk = K >> 2;
-  const int NG = K / G;
+  const int KT = (K + 127) >> 7;
   const int lane = threadIdx.x & 63;
   for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
     const int c = c0 + threadIdx.x;
@@ -155,28 +224,40 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restri
     const int q1 = clamp_i((int)rintf(e1 / s) + z, 0, 15);
     const int q2 = clamp_i((int)rintf(e2 / s) + z, 0, 15);
     const int q3 = clamp_i((int)rintf(e3 / s) + z, 0, 15);
+    // codes k = 4c..4c+3 go to the low (c even) or high (c odd) nibbles of
+    // bytes 0..3 of the word covering k0 = 8*(c/2): pair adjacent lanes.
+    const u32 spread = (u32)q0 | ((u32)q1 << 8) | ((u32)q2 << 16) | ((u32)q3 << 24);
+    const u32 other = (u32)lane_xor<1>((int)spread);
     const int gi = c / LPG;
     const bool leader = (lane % LPG) == 0;
     int z_next = 0;
     if constexpr (Z4) z_next = lane_xor<LPG>(z);  // zero of the odd partner group
     if (valid) {
-      const uint16_t packed = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
-      reinterpret_cast<uint16_t*>(wq + (size_t)n * (K >> 1))[c] = packed;
+      if ((c & 1) == 0)
+        *reinterpret_cast<u32*>(wq + w4_word_offset(n, 4 * c, KT)) = spread | (other << 4);
       if (leader) {
-        w_scale[(size_t)n * NG + gi] = __half_as_ushort(sh);
+        const size_t pi = w4_param_index(n, gi, KB, GPB);
+        w_scale[pi] = __half_as_ushort(sh);
         if constexpr (Z4) {
+          // pairs (2c, 2c+1) of a block share a byte; the next group of a
+          // block is the next group of the row (blocks hold whole pairs)
           if ((gi & 1) == 0) {
-            const int zo = (gi + 1 < NG) ? z_next : 0;
-            reinterpret_cast<uint8_t*>(w_zero)[(size_t)n * ((NG + 1) >> 1) + (gi >> 1)] =
-                (uint8_t)(z | (zo << 4));
+            const int zo = (gi + 1 < K / G) ? z_next : 0;
+            reinterpret_cast<uint8_t*>(w_zero)[pi >> 1] = (uint8_t)(z | (zo << 4));
           }
         } else {
-          reinterpret_cast<uint16_t*>(w_zero)[(size_t)n * NG + gi] =
-              __half_as_ushort(__int2half_rn(z));
+          reinterpret_cast<uint16_t*>(w_zero)[pi] = __half_as_ushort(__int2half_rn(z));
         }
       }
     }
   }
+}
+
+// Byte offset of codes k..k+3 (k % 4 == 0) of row n in the tiled W8 layout:
+// tiles of 16 rows x 64 k; piece 16*b + r holds row r's k in [16b, 16b+16).
+SVG_DEV size_t w8_offset(int n, int k, int KT8) {
+  const int i = n >> 4, r = n & 15, j = k >> 6, kc = k & 63;
+  return ((size_t)i * KT8 + j) * 1024 + (size_t)(16 * (kc >> 4) + r) * 16 + (kc & 15);
 }
 
 __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restrict__ W, int K,
@@ -188,6 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restri
   const int n = blockIdx.x;
   const float* row = W + (size_t)n * K;
   const int nchunk = K >> 2;
+  const int KT8 = (K + 63) >> 6;
   float amax = 0.f;
   for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
     const int c = c0 + threadIdx.x;
@@ -205,7 +287,6 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restri
   if (__half_as_ushort(sh) == 0) sh = __ushort_as_half(0x3C00);
   const float s = __half2float(sh);
   if (threadIdx.x == 0) w_scale[n] = __half_as_ushort(sh);
-  int8_t* out = wq + (size_t)n * K;
   for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
     const int c = c0 + threadIdx.x;
     const bool valid = c < nchunk;
@@ -216,23 +297,59 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restri
       const int q1 = clamp_i((int)rintf(e1 / s), -127, 127);
       const int q2 = clamp_i((int)rintf(e2 / s), -127, 127);
       const int q3 = clamp_i((int)rintf(e3 / s), -127, 127);
-      *reinterpret_cast<u32*>(out + 4 * c) = (u32)(q0 & 0xFF) | ((u32)(q1 & 0xFF) << 8) |
-                                             ((u32)(q2 & 0xFF) << 16) | ((u32)(q3 & 0xFF) << 24);
+      *reinterpret_cast<u32*>(wq + w8_offset(n, 4 * c, KT8)) =
+          (u32)(q0 & 0xFF) | ((u32)(q1 & 0xFF) << 8) | ((u32)(q2 & 0xFF) << 16) | ((u32)(q3 & 0xFF) << 24);
     }
   }
+}
+
+// Zero-fill of a 4-byte-aligned byte range (the padding of the tiled layouts);
+// a kernel rather than a memset so that a captured graph replays it safely.
+__global__ __launch_bounds__(kThreads) void k_fill_zero(u32* __restrict__ p, size_t nwords) {
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < nwords; i += (size_t)gridDim.x * kThreads)
+    p[i] = 0u;
 }
 
 }  // namespace
 
 hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int8_t* xq,
                                     float* x_scale, hipStream_t stream) {
-  hipLaunchKernelGGL(k_act_rht_quant, dim3(M), dim3(kThreads), 0, stream, X, K, signs, xq, x_scale);
+  const int cpt = (K / 4 + kThreads - 1) / kThreads;  // float4 chunks per thread
+  const dim3 grid(M), block(kThreads);
+  if (cpt <= 1)
+    hipLaunchKernelGGL((k_act_rht_quant_reg<1>), grid, block, 0, stream, X, K, signs, xq, x_scale);
+  else if (cpt <= 2)
+    hipLaunchKernelGGL((k_act_rht_quant_reg<2>), grid, block, 0, stream, X, K, signs, xq, x_scale);
+  else if (cpt <= 4)
+    hipLaunchKernelGGL((k_act_rht_quant_reg<4>), grid, block, 0, stream, X, K, signs, xq, x_scale);
+  else if (cpt <= 8)
+    hipLaunchKernelGGL((k_act_rht_quant_reg<8>), grid, block, 0, stream, X, K, signs, xq, x_scale);
+  else if (cpt <= 16)
+    hipLaunchKernelGGL((k_act_rht_quant_reg<16>), grid, block, 0, stream, X, K, signs, xq, x_scale);
+  else
+    hipLaunchKernelGGL(k_act_rht_quant, grid, block, 0, stream, X, K, signs, xq, x_scale);
+  return hipGetLastError();
+}
+
+static hipError_t fill_zero(void* p, size_t nbytes, hipStream_t stream) {
+  const size_t nwords = nbytes / 4;
+  const unsigned blocks = (unsigned)((nwords + kThreads - 1) / kThreads < 1024 ? (nwords + kThreads - 1) / kThreads : 1024);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(kThreads), 0, stream, reinterpret_cast<u32*>(p), nwords);
   return hipGetLastError();
 }
 
 hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* signs, int group,
                                    bool z4, uint8_t* wq, uint16_t* w_scale, void* w_zero,
                                    float* w_rot, hipStream_t stream) {
+  if (N % 16 || K % kMetaK) {  // the tiled/blocked storage has padding: clear it first
+    size_t wb, sb, zb;
+    svg_w4_storage(N, K, group, z4, &wb, &sb, &zb);
+    hipError_t e;
+    if ((e = fill_zero(wq, wb, stream)) != hipSuccess) return e;
+    if ((e = fill_zero(w_scale, sb, stream)) != hipSuccess) return e;
+    if ((e = fill_zero(w_zero, zb, stream)) != hipSuccess) return e;
+  }
   const dim3 grid(N), block(kThreads);
 #define SVG_W4_CASE(G)                                                                            \
   if (group == G) {                                                                               \
@@ -253,6 +370,12 @@ hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* s
 
 hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* signs, int8_t* wq,
                                    uint16_t* w_scale, float* w_rot, hipStream_t stream) {
+  if (N % 16 || K % 64) {
+    size_t wb, sb;
+    svg_w8_storage(N, K, &wb, &sb);
+    hipError_t e = fill_zero(wq, wb, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_rot_quant_w8, dim3(N), dim3(kThreads), 0, stream, W, K, signs, wq, w_scale,
                      w_rot);
   return hipGetLastError();

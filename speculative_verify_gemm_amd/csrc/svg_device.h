@@ -95,4 +95,55 @@ SVG_DEV uint4 load_nt16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 SVG_DEV uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
 SVG_DEV float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// Raw buffer loads.  A buffer resource covers [base, base + nbytes); a load
+// whose offset lies outside returns zeros instead of faulting, which makes
+// ragged tails branch-free: an out-of-range lane passes kOOB as its offset.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr u32 kOOB = 0x80000000u;      // beyond every buffer this library builds
+constexpr int kNT = 2;                 // cache policy: non-temporal (streamed once)
+SVG_DEV rsrc_t make_rsrc(const void* base, u32 nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
+}
+SVG_DEV u32x4 bload16(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+SVG_DEV u32x4 bload16_nt(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT); }
+SVG_DEV u32 bload4(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+SVG_DEV uint16_t bload2(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+SVG_DEV uint8_t bload1(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
+
+// NB contiguous bytes (NB in 1, 2, 4, 8, 16, 32) from an NB-aligned offset
+// (16-aligned for 32), as little-endian 32-bit words.
+template <int NB>
+struct Bytes {
+  u32 w[NB >= 4 ? NB / 4 : 1];
+};
+template <int NB>
+SVG_DEV void bload_bytes(Bytes<NB>& o, rsrc_t r, u32 off) {
+  if constexpr (NB == 32) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u, 0, 0);
+    for (int i = 0; i < 4; ++i) { o.w[i] = a[i]; o.w[4 + i] = b[i]; }
+  } else if constexpr (NB == 16) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    for (int i = 0; i < 4; ++i) o.w[i] = a[i];
+  } else if constexpr (NB == 8) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    o.w[0] = a[0];
+    o.w[1] = a[1];
+  } else if constexpr (NB == 4) {
+    o.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (NB == 2) {
+    o.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else {
+    o.w[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+  }
+}
+// The i-th fp16 of a block of words, as float.
+SVG_DEV float half_at(const u32* w, int i) {
+  return half_bits_to_float((uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFF)));
+}
+// The i-th 4-bit value of a block of words.
+SVG_DEV int nibble_at(const u32* w, int i) { return (int)((w[i >> 3] >> (4 * (i & 7))) & 0xF); }

@@ -19,5 +19,27 @@ hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg,
                            hipStream_t stream);
 
+// Bytes of the weight storage (include/svgemm.h describes the layout).
+// W4 codes: tiled, rows padded to 16 and K to 128.  Scales and zeros:
+// blocked per (16-row tile, 512-k block, row), rows padded to 16 and K to
+// 512.  W8 codes: tiled, rows padded to 16, K to 64; scales [N].
+constexpr int kMetaK = 512;
+inline void svg_w4_storage(int N, int K, int group, bool z4, size_t* wq_bytes, size_t* scale_bytes,
+                           size_t* zero_bytes) {
+  const size_t Np = (size_t)(N + 15) / 16 * 16, KT = (size_t)(K + 127) / 128;
+  const size_t Gp = (size_t)(K + kMetaK - 1) / kMetaK * (kMetaK / group);  // padded groups per row
+  *wq_bytes = Np * KT * 64;
+  *scale_bytes = Np * Gp * 2;
+  *zero_bytes = z4 ? Np * Gp / 2 : Np * Gp * 2;
+}
+inline void svg_w8_storage(int N, int K, size_t* wq_bytes, size_t* scale_bytes) {
+  const size_t Np = (size_t)(N + 15) / 16 * 16, KT = (size_t)(K + 63) / 64;
+  *wq_bytes = Np * KT * 64;
+  *scale_bytes = (size_t)N * 2;
+}
+
+// Compute units of the current device (cached per device id).
+int svg_cu_count();
+
 // Largest M served by the dot-product (GEMV) kernels; larger M use MFMA.
 constexpr int kGemvMaxM = 2;

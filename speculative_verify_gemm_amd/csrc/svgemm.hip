@@ -40,9 +40,43 @@ constexpr int kMaxKW8 = 131072;  // 127^2 * K < 2^31
 
 }  // namespace
 
+int svg_cu_count() {
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (counts[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 1;
+    counts[dev] = c;
+  }
+  return counts[dev];
+}
+
 extern "C" {
 
 const char* svg_last_error(void) { return g_last_error.c_str(); }
+
+svg_status svg_weight_sizes(int N, int K, int fmt, int group, uint64_t* wq_bytes,
+                            uint64_t* scale_bytes, uint64_t* zero_bytes) {
+  static const char* fn = "svg_weight_sizes";
+  if (N < 0 || K <= 0) return fail(SVG_EINVAL, fn, "N < 0 or K <= 0");
+  if (!wq_bytes || !scale_bytes || !zero_bytes) return fail(SVG_EINVAL, fn, "null output pointer");
+  if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16 && fmt != SVG_W8_SYM)
+    return fail(SVG_EUNSUPPORTED, fn, "unknown fmt");
+  if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  size_t w, sc, z = 0;
+  if (fmt == SVG_W8_SYM) {
+    svg_w8_storage(N, K, &w, &sc);
+  } else {
+    if (!group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
+    if (K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of group");
+    svg_w4_storage(N, K, group, fmt == SVG_W4_ASYM_Z4, &w, &sc, &z);
+  }
+  *wq_bytes = w;
+  *scale_bytes = sc;
+  *zero_bytes = z;
+  return ok();
+}
 
 svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs, int block, int fmt,
                               int group, void* wq, uint16_t* w_scale, void* w_zero,
@@ -61,8 +95,8 @@ svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
     return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(W, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "W and wq need 16-byte alignment");
   if (!aligned(signs, 4)) return fail(SVG_EALIGN, fn, "signs needs 4-byte alignment");
-  if (!aligned(w_scale, 2) || (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 2)))
-    return fail(SVG_EALIGN, fn, "w_scale / fp16 w_zero need 2-byte alignment");
+  if (!aligned(w_scale, 4) || (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 4)))
+    return fail(SVG_EALIGN, fn, "w_scale / fp16 w_zero need 4-byte alignment");
   if (w_rot_debug && !aligned(w_rot_debug, 16)) return fail(SVG_EALIGN, fn, "w_rot_debug needs 16-byte alignment");
   if (N == 0) return ok();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -103,8 +137,8 @@ svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
   if (!xq || !x_scale || !wq || !w_scale || !w_zero || !y) return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "xq and wq need 16-byte alignment");
-  if (!aligned(x_scale, 4) || !aligned(y, 4) || !aligned(w_scale, 2) ||
-      (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 2)) || (partials_debug && !aligned(partials_debug, 4)))
+  if (!aligned(x_scale, 4) || !aligned(y, 4) || !aligned(w_scale, 4) ||
+      (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 4)) || (partials_debug && !aligned(partials_debug, 4)))
     return fail(SVG_EALIGN, fn, "misaligned scale, zero, y or partials pointer");
   if (M == 0 || N == 0) return ok();
   return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,

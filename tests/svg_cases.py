@@ -31,11 +31,16 @@ def gpu_quant_acts(x, signs):
     return xq, xs
 
 
-def gpu_prepare(W, signs, fmt, group, debug=False):
-    """W: numpy [N,K] fp32 or a device tensor."""
+def gpu_prepare(W, signs, fmt, group, debug=False, poison=True):
+    """W: numpy [N,K] fp32 or a device tensor.  The storage is first filled
+    with a non-zero byte so that padding the library fails to write shows."""
     Wd = W if isinstance(W, torch.Tensor) else to_dev(W)
     N, K = Wd.shape
     wq, ws, wz = svg.empty_weights(N, K, fmt, group)
+    if poison:
+        for t in (wq, ws, wz):
+            if t is not None:
+                t.view(torch.uint8).fill_(0x5A)
     rot = torch.empty((N, K), dtype=torch.float32, device=DEV) if debug else None
     svg.rht_rotate_weights(Wd, to_dev(signs), fmt, group, wq, ws, wz, rot)
     return dict(wq=wq, ws=ws, wz=wz, rot=rot, fmt=fmt, group=group, N=N, K=K)
@@ -47,22 +52,29 @@ def gpu_linear(xq, xs, w, debug=True):
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)
     if w["fmt"] == "w8":
         dbg = torch.empty((M, N), dtype=torch.int32, device=DEV) if debug else None
-        svg.w8a8_linear(xq, xs, w["wq"], w["ws"], y, dbg)
+        svg.w8a8_linear(xq, xs, w["wq"], w["ws"], N, y, dbg)
     else:
         dbg = torch.empty((M, N, K // w["group"]), dtype=torch.int32, device=DEV) if debug else None
-        svg.w4a8_linear(xq, xs, w["wq"], w["ws"], w["wz"], w["fmt"], w["group"], y, dbg)
+        svg.w4a8_linear(xq, xs, w["wq"], w["ws"], w["wz"], w["fmt"], w["group"], N, y, dbg)
     return y, dbg
+
+
+def oracle_storage(ow, fmt, K):
+    """The oracle's encoded weights in the library's tiled storage (host arrays)."""
+    from oracle import svg_oracle as O
+    if fmt == "w8":
+        return O.pack_w8_codes(ow["q"]), ow["s"], None
+    g = ow["group"]
+    z = O.pack_z4(ow["z"], K, g) if fmt == "w4_z4" else O.zeros_as_f16(ow["z"], K, g)
+    return O.pack_w4_codes(ow["q"]), O.tile_group_params(ow["s"], K, g), z
 
 
 def oracle_weights_to_dev(ow, fmt):
     """Device copies of the oracle's encoded weights, in the library layout."""
-    from oracle import svg_oracle as O
-    if fmt == "w8":
-        return dict(wq=to_dev(ow["q"]), ws=to_dev(ow["s"]), wz=None, fmt=fmt, group=0,
-                    N=ow["q"].shape[0], K=ow["q"].shape[1])
-    z = O.pack_z4(ow["z"]) if fmt == "w4_z4" else O.zeros_as_f16(ow["z"])
-    return dict(wq=to_dev(O.pack_w4_codes(ow["q"])), ws=to_dev(ow["s"]), wz=to_dev(z), fmt=fmt,
-                group=ow["group"], N=ow["q"].shape[0], K=ow["q"].shape[1])
+    N, K = ow["q"].shape
+    wq, ws, wz = oracle_storage(ow, fmt, K)
+    return dict(wq=to_dev(wq), ws=to_dev(ws), wz=None if wz is None else to_dev(wz), fmt=fmt,
+                group=ow.get("group", 0), N=N, K=K)
 
 
 def host(t):

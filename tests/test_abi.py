@@ -29,7 +29,8 @@ def svg():
 
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
-        ["act_rht_quant_i8", "rht_rotate_weights", "svg_last_error", "w4a8_linear", "w8a8_linear"])
+        ["act_rht_quant_i8", "rht_rotate_weights", "svg_last_error", "svg_weight_sizes",
+         "w4a8_linear", "w8a8_linear"])
 
 
 def test_library_exports_every_declared_symbol(svg):
@@ -104,6 +105,25 @@ def test_rotate_validation(svg, args, code):
 ])
 def test_w8a8_validation(svg, args, code):
     assert svg.lib.w8a8_linear(*args, NULL) == code
+
+
+def test_weight_sizes_match_the_oracle_layout(svg):
+    import numpy as np
+    from oracle import svg_oracle as O
+    for N, K, fmt, g in [(37, 384, "w4_z4", 32), (12288, 4096, "w4_z16", 64), (20, 384, "w4_z16", 128), (20, 320, "w4_z16", 64),
+                         (5, 96, "w4_z4", 32), (45, 1120, "w8", 0), (16, 64, "w8", 0)]:
+        wb, sb, zb = svg.weight_sizes(N, K, fmt, g)
+        if fmt == "w8":
+            assert wb == O.pack_w8_codes(np.zeros((N, K), np.int8)).nbytes and sb == 2 * N and zb == 0
+        else:
+            q = np.zeros((N, K), np.uint8)
+            z = np.zeros((N, K // g), np.uint8)
+            assert wb == O.pack_w4_codes(q).nbytes
+            assert sb == O.tile_group_params(z.astype(np.float16), K, g).nbytes
+            zref = O.pack_z4(z, K, g) if fmt == "w4_z4" else O.zeros_as_f16(z, K, g)
+            assert zb == zref.nbytes
+    with pytest.raises(svg.SvgError):
+        svg.weight_sizes(16, 48, "w4_z16", 64)
 
 
 def test_binding_has_no_cpu_path(svg):

@@ -232,11 +232,84 @@ def test_w8_quant_bounds():
     assert np.all(np.abs(s64[ok] - a[ok] / 127) <= 2.0 ** -11 * s64[ok] * 1.001)
 
 
-def test_pack_layout_by_hand():
-    q = np.array([[1, 2, 3, 4, 15, 0, 7, 8]], dtype=np.uint8)
-    assert O.pack_w4_codes(q).tolist() == [[0x21, 0x43, 0x0F, 0x87]]
-    z = np.array([[3, 12, 5]], dtype=np.uint8)
-    assert O.pack_z4(z).tolist() == [[0xC3, 0x05]]
+def _w4_byte_and_nibble(n, k, K):
+    """The byte offset and nibble (0 = low) of code (n, k) by the layout rule
+    written out element by element."""
+    KT = -(-K // 128)
+    i, r = n // 16, n % 16
+    j, kc = k // 128, k % 128
+    h, b = kc // 64, (kc % 64) // 16
+    w, t8 = (kc % 16) // 8, kc % 8
+    return (i * KT + j) * 1024 + (16 * b + r) * 16 + h * 8 + w * 4 + t8 % 4, t8 // 4
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 256), (37, 96), (20, 320)])
+def test_w4_tiled_layout_element_by_element(N, K):
+    rng = np.random.default_rng(N * K)
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    packed = O.pack_w4_codes(q)
+    Np, Kp = O.w4_tiled_shape(N, K)
+    assert packed.size == Np * Kp // 2
+    seen = np.zeros(packed.size * 2, bool)
+    for n in range(N):
+        for k in range(K):
+            off, e = _w4_byte_and_nibble(n, k, K)
+            assert (packed[off] >> (4 * e)) & 0xF == q[n, k]
+            seen[2 * off + e] = True
+    # everything not holding a code is zero padding
+    flat = np.stack([packed & 0xF, packed >> 4], axis=1).reshape(-1)
+    assert not flat[~seen].any()
+
+
+def test_w4_tiled_layout_worked_example():
+    # row 0, k = 0..127 with code k % 16: piece 0 holds k 0..15 then 64..79.
+    q = (np.arange(128) % 16).astype(np.uint8)[None, :]
+    p = O.pack_w4_codes(q)
+    assert p[:8].tolist() == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
+    assert p[8:16].tolist() == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
+    assert not p[16:256].any()          # pieces of rows 1..15 (padding)
+
+
+@pytest.mark.parametrize("N,K,group", [(16, 512, 64), (37, 384, 32), (20, 1024, 128), (5, 320, 64),
+                                        (33, 1536, 128)])
+def test_group_params_blocked_element_by_element(N, K, group):
+    rng = np.random.default_rng(7)
+    G = K // group
+    a = rng.integers(1, 1000, size=(N, G)).astype(np.float16)
+    z = rng.integers(0, 16, size=(N, G)).astype(np.uint8)
+    t = O.tile_group_params(a, K, group)
+    z4 = O.pack_z4(z, K, group)
+    gpb = 512 // group
+    KB = -(-K // 512)
+    Np = -(-N // 16) * 16
+    assert t.size == Np * KB * gpb and z4.size * 2 == t.size
+    for n in range(N):
+        for g in range(G):
+            i, r, jb, c = n // 16, n % 16, g // gpb, g % gpb
+            idx = ((i * KB + jb) * 16 + r) * gpb + c
+            assert t[idx] == a[n, g]
+            assert (z4[idx // 2] >> (4 * (idx % 2))) & 0xF == z[n, g]
+    assert np.count_nonzero(t) == N * G
+
+
+def test_z4_pack_by_hand():
+    z = np.zeros((1, 8), dtype=np.uint8)
+    z[0, :3] = [3, 12, 5]
+    p = O.pack_z4(z, 512, 64)
+    assert p[:2].tolist() == [0xC3, 0x05] and not p[2:].any()
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (21, 96), (3, 200 - 200 % 32)])
+def test_w8_tiled_layout_element_by_element(N, K):
+    rng = np.random.default_rng(N + K)
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    p = O.pack_w8_codes(q)
+    KT = -(-K // 64)
+    for n in range(N):
+        for k in range(K):
+            i, r, j, kc = n // 16, n % 16, k // 64, k % 64
+            assert p[(i * KT + j) * 1024 + (16 * (kc // 16) + r) * 16 + kc % 16] == q[n, k]
+    assert np.count_nonzero(p) == np.count_nonzero(q)
 
 
 # ------------------------------------------------------- contraction pins
@@ -319,15 +392,18 @@ def test_byte_ceiling_worked_example(golden_dir):
 
 @pytest.mark.parametrize("fmt,group", [("w4_z4", 32), ("w4_z16", 64), ("w4_z16", 128), ("w8", 0)])
 def test_linear_bytes_counts_real_arrays(fmt, group):
-    M, N, K = 5, 24, 384
+    # shapes without tile padding (N % 16 == 0, K % 256 == 0): the stored
+    # arrays then hold exactly the algorithmic bytes
+    M, N, K = 5, 32, 512
     x, W, signs = synth.random_case(M, N, K, seed=1)
     if fmt == "w8":
         w = O.prepare_w8(W, signs)
-        wbytes = w["q"].nbytes + w["s"].nbytes
+        wbytes = O.pack_w8_codes(w["q"]).nbytes + w["s"].nbytes
     else:
         w = O.prepare_w4(W, signs, group)
-        z = O.pack_z4(w["z"]) if fmt == "w4_z4" else O.zeros_as_f16(w["z"])
-        wbytes = O.pack_w4_codes(w["q"]).nbytes + w["s"].nbytes + z.nbytes
+        z = O.pack_z4(w["z"], K, group) if fmt == "w4_z4" else O.zeros_as_f16(w["z"], K, group)
+        wbytes = (O.pack_w4_codes(w["q"]).nbytes + O.tile_group_params(w["s"], K, group).nbytes
+                  + z.nbytes)
     qx, sx = O.quant_acts(x, signs)
     y = np.zeros((M, N), np.float32)
     assert O.linear_bytes(M, N, K, fmt, group) == wbytes + qx.nbytes + sx.nbytes + y.nbytes

@@ -73,15 +73,15 @@ def test_weight_codes_bit_exact(fmt, group, N, K):
     assert np.array_equal(C.host(w["rot"]).view(np.uint32), u.view(np.uint32))
     if fmt == "w8":
         q, s = O.quant_w8(u)
-        assert np.array_equal(C.host(w["wq"]), q)
-        assert np.array_equal(C.host(w["ws"]).view(np.uint16), s.view(np.uint16))
+        ow = dict(q=q, s=s)
     else:
         q, s, z = O.quant_w4(u, group)
-        assert np.array_equal(C.host(w["wq"]), O.pack_w4_codes(q))
-        assert np.array_equal(C.host(w["ws"]).view(np.uint16), s.view(np.uint16))
-        zref = O.pack_z4(z) if fmt == "w4_z4" else O.zeros_as_f16(z).view(np.uint16)
-        zgot = C.host(w["wz"])
-        assert np.array_equal(zgot if fmt == "w4_z4" else zgot.view(np.uint16), zref)
+        ow = dict(q=q, s=s, z=z, group=group)
+    wq, ws, wz = C.oracle_storage(ow, fmt, K)
+    assert np.array_equal(C.host(w["wq"]).view(np.uint8), wq.view(np.uint8).reshape(-1))
+    assert np.array_equal(C.host(w["ws"]).view(np.uint16), ws.view(np.uint16).reshape(-1))
+    if wz is not None:
+        assert np.array_equal(C.host(w["wz"]).view(np.uint8), wz.view(np.uint8).reshape(-1))
 
 
 # ----------------------------------------------------------------- linear
@@ -138,9 +138,9 @@ def test_end_to_end_and_deterministic(fmt, group, M):
     buf = torch.full((pad + M * N + pad,), 12345.0, dtype=torch.float32, device=C.DEV)
     yv = buf[pad:pad + M * N].view(M, N)
     if fmt == "w8":
-        svg.w8a8_linear(xq, xs, w["wq"], w["ws"], yv)
+        svg.w8a8_linear(xq, xs, w["wq"], w["ws"], N, yv)
     else:
-        svg.w4a8_linear(xq, xs, w["wq"], w["ws"], w["wz"], fmt, group, yv)
+        svg.w4a8_linear(xq, xs, w["wq"], w["ws"], w["wz"], fmt, group, N, yv)
     b = C.host(buf)
     assert np.all(b[:pad] == 12345.0) and np.all(b[pad + M * N:] == 12345.0)
     assert np.array_equal(b[pad:pad + M * N].view(np.uint32), C.host(y1).reshape(-1).view(np.uint32))
@@ -159,6 +159,8 @@ def test_full_size_single_matrix(src):
     y, dbg = C.gpu_linear(xq, xs, w)
     assert np.array_equal(C.host(xq), qx)
     assert np.array_equal(C.host(w["wq"]), O.pack_w4_codes(ow["q"]))
+    assert np.array_equal(C.host(w["ws"]).view(np.uint16),
+                          O.tile_group_params(ow["s"], x.shape[1], g).view(np.uint16))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
 
@@ -167,11 +169,11 @@ def test_rejects_bad_arguments_without_writing():
     import speculative_verify_gemm_amd as svg
     xq = torch.zeros((2, 64), dtype=torch.int8, device=C.DEV)
     xs = torch.ones(2, dtype=torch.float32, device=C.DEV)
-    wq = torch.zeros((8, 32), dtype=torch.uint8, device=C.DEV)
-    ws = torch.ones((8, 1), dtype=torch.float16, device=C.DEV)
-    wz = torch.zeros((8, 1), dtype=torch.float16, device=C.DEV)
+    wq = torch.zeros((16 * 64,), dtype=torch.uint8, device=C.DEV)
+    ws = torch.ones((32,), dtype=torch.float16, device=C.DEV)
+    wz = torch.zeros((32,), dtype=torch.float16, device=C.DEV)
     y = torch.full((2, 8), 7.0, device=C.DEV)
     with pytest.raises(svg.SvgError) as ei:
-        svg.w4a8_linear(xq, xs, wq, ws, wz, "w4_z16", 48, y)
+        svg.w4a8_linear(xq, xs, wq, ws, wz, "w4_z16", 48, 8, y)
     assert ei.value.status == svg.SVG_EUNSUPPORTED
     assert torch.all(y == 7.0)
