@@ -165,75 +165,134 @@ class Stack:
 
 
 def time_graph(torch, g, steps, warmup, dev):
+    """Replay the captured pass: `warmup` untimed, then `steps` timed between
+    HIP events on the replay stream.  Returns (mean, median, min) ms per pass;
+    the mean is the whole timed region / steps."""
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize(dev)
-    return e0.elapsed_time(e1) / steps  # ms per pass
+    per = sorted(a.elapsed_time(b) for a, b in zip(ev, ev[1:]))
+    return ev[0].elapsed_time(ev[-1]) / steps, per[len(per) // 2], per[0]
 
 
-def time_linear_launches(stack, io, steps):
-    """Per-launch duration of the linear kernel, from HIP events recorded on
-    the stream it is launched on (eager passes)."""
+def time_linear_launches(stack, io, g, ms_graph, steps):
+    """Mean duration of the linear launches, from HIP events recorded on the
+    stream they run on.  For each launch kind of a layer (qkv, o, gate/up,
+    down) the launches of all layers run back to back between two events (the
+    activations quantized once before, untimed), so the event overhead spreads
+    over `layers` launches and each launch counts from the end of the previous
+    one to its own end -- the same span a kernel trace reports.  Before each
+    step the captured pass is replayed enough times to keep the device busy
+    while the host enqueues, so no host launch latency enters the timed spans.
+    Returns (mean ms, mean algorithmic bytes, launches, {kind: mean us})."""
     torch = stack.torch
-    per_pass = stack.layers * len(LAYER_LAUNCHES)
-    durs = []
-    bytes_per_launch = [linear_bytes(io["M"], N, K, stack.fmt, stack.group)
-                        for _L in range(stack.layers) for _n, _m, N, K, _s in LAYER_LAUNCHES]
+    t0 = time.perf_counter()
+    stack.run_pass(io)                       # host cost of enqueuing one eager pass
+    enqueue_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize(stack.dev)
+    blockers = max(2, int(2.0 * enqueue_ms / ms_graph) + 1)
+    per_kind = {name: [] for name, *_ in LAYER_LAUNCHES}
     for _ in range(steps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(per_pass)]
-        order = list(evs)
-        stack.run_pass(io, events=list(reversed(evs)))
+        for _ in range(blockers):
+            g.replay()
+        spans = []
+        for name, _m, _N, _K, space in LAYER_LAUNCHES:
+            stack.svg.act_rht_quant_i8(io["xin"][0][space], stack.signs[0][space], io["xq"][space],
+                                       io["xs"][space])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for L in range(stack.layers):
+                stack.linear(io, L, name, space)
+            e1.record()
+            spans.append((name, e0, e1))
         torch.cuda.synchronize(stack.dev)
-        durs.extend(a.elapsed_time(b) for a, b in order)
-    mean_ms = sum(durs) / len(durs)
-    mean_bytes = sum(bytes_per_launch) / len(bytes_per_launch)
-    return mean_ms, mean_bytes, len(durs)
+        for name, e0, e1 in spans:
+            per_kind[name].append(e0.elapsed_time(e1) / stack.layers)
+    mean_kind = {n: sum(v) / len(v) for n, v in per_kind.items()}
+    mean_ms = sum(mean_kind.values()) / len(mean_kind)
+    nbytes = [linear_bytes(io["M"], N, K, stack.fmt, stack.group) for _n, _m, N, K, _s in LAYER_LAUNCHES]
+    return (mean_ms, sum(nbytes) / len(nbytes), steps * stack.layers * len(LAYER_LAUNCHES),
+            {n: round(v * 1e3, 3) for n, v in mean_kind.items()})
 
 
 def kernel_name(fmt, group, M):
-    if M <= 2:
-        return "k_w8a8_dot" if fmt == "w8" else "k_w4a8_dot"
-    return "k_w8a8_mfma" if fmt == "w8" else "k_w4a8_mfma"
+    """The linear kernel template instance a launch of this format and M runs
+    (k_linear<policy, waves, chunks per wave, batch>; the shape varies with K)."""
+    if fmt == "w8":
+        pol = f"DotW8<{M}>" if M <= 2 else f"MfmaW8<{1 if M <= 16 else 2}>"
+    else:
+        z4 = "true" if fmt == "w4_z4" else "false"
+        if M <= 2 or group == 32:
+            pol = f"DotW4<{1 if M <= 1 else 2 if M <= 2 else 8}, {group}, {z4}, false>"
+        else:
+            pol = f"MfmaW4<{1 if M <= 16 else 2}, {group}, {z4}, false>"
+    return f"k_linear<{pol}, ...>"
 
 
-def cpu_baseline(stack, M):
-    """The CPU oracle on layer 0 of the same workload (the four launches of
-    one layer, all rows): weights copied from the device generator and encoded
-    by the oracle (untimed), then the per-pass steps (activation rotation and
-    quantization, integer contraction, fp64 output) timed."""
+def profiled_traffic(workload, M):
+    """HBM bytes per linear launch measured by rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE, each scaled by its reading for a copy of known size), from the
+    committed summary for this workload -- or None when there is none or the
+    kernels have changed since it was taken (its source digest differs)."""
+    import re
+    from speculative_verify_gemm_amd.build import source_digest
+    path = os.path.join(ROOT, "profiles", f"linear_{workload}_m{M}_traffic.md")
+    if not os.path.exists(path):
+        return None, None
+    text = open(path).read()
+    dig = re.search(r"^digest: (\w+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch: ([0-9.eE+]+)", text, re.M)
+    if not dig or not val:
+        return None, None
+    if dig.group(1) != source_digest():
+        return None, "stale"
+    return float(val.group(1)), os.path.relpath(path, ROOT)
+
+
+def cpu_baseline(stack, M, min_seconds=12.0, max_reps=32):
+    """The CPU oracle on a bounded sample of the same workload: the four
+    launches of layer 0 (weights copied from the device generator and encoded
+    by the oracle, untimed), run on the activations of layers 0, 1, 2, ...
+    until at least `min_seconds` of CPU time have been spent.  Timed: the
+    per-pass steps (activation rotation and quantization, exact integer
+    contraction, fp64 output), single-threaded."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     synth = stack.synth
     from oracle import svg_oracle as O
-    L = 0
     prepared = []
     for name, members, N, K, space in LAYER_LAUNCHES:
-        Ws = [synth.stack_weight(L, m, device=stack.dev).cpu().numpy() for m in members]
+        Ws = [synth.stack_weight(0, m, device=stack.dev).cpu().numpy() for m in members]
         W = np.concatenate(Ws, axis=0)
-        signs = synth.stack_signs(L, space)
+        signs = synth.stack_signs(0, space)
         ow = O.prepare_w8(W, signs) if stack.fmt == "w8" else O.prepare_w4(W, signs, stack.group)
-        x = synth.stack_acts(stack.wl, L, space, M)
-        prepared.append((x, signs, ow, N, K))
+        prepared.append((space, signs, ow, N, K))
         del W, Ws
-    t0 = time.perf_counter()
-    for x, signs, ow, N, K in prepared:
-        if stack.fmt == "w8":
-            O.linear_w8(x, signs, ow)
-        else:
-            O.linear_w4(x, signs, ow)
-    dt = time.perf_counter() - t0
-    nbytes = sum(linear_bytes(M, N, K, stack.fmt, stack.group) for _x, _s, _o, N, K in prepared)
+    layer_bytes = sum(linear_bytes(M, N, K, stack.fmt, stack.group) for _sp, _s, _o, N, K in prepared)
+    dt, reps = 0.0, 0
+    with threadpool_limits(limits=1):
+        while reps < max_reps and (reps == 0 or dt < min_seconds):
+            xs = [synth.stack_acts(stack.wl, reps, sp, M) for sp, _s, _o, _N, _K in prepared]
+            t0 = time.perf_counter()
+            for x, (sp, signs, ow, N, K) in zip(xs, prepared):
+                if stack.fmt == "w8":
+                    O.linear_w8(x, signs, ow)
+                else:
+                    O.linear_w4(x, signs, ow)
+            dt += time.perf_counter() - t0
+            reps += 1
+    nbytes = layer_bytes * reps
     return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"layer 0 of the same stack (qkv, o, gate/up, down; {nbytes / 1e6:.1f} MB of "
-                       f"algorithmic bytes) at M={M}: activation RHT + int8 quantization, exact "
-                       f"integer contraction, fp64 output; numpy, single thread; {dt:.2f} s",
+                sample=f"the four launches of layer 0 (qkv, o, gate/up, down; {layer_bytes / 1e6:.1f} MB of "
+                       f"algorithmic bytes each time) on the activations of {reps} layers at M={M}: "
+                       f"activation RHT + int8 quantization, exact integer contraction, fp64 output; "
+                       f"numpy, one thread; {dt:.1f} s timed",
                 seconds=dt, cpu=platform.processor() or platform.machine())
 
 
@@ -248,6 +307,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the M=1 comparison pass")
     ap.add_argument("--sweep", default=None, help="comma-separated M values: report a pass per M")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first copy this many MiB device to device (three times): the copy of known "
+                         "size that scales the HBM byte counters of a profiling run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -255,27 +317,41 @@ def main():
         sys.exit(2)
 
     import torch
+    from speculative_verify_gemm_amd.build import source_digest
     dev = torch.device("cuda:0")
     spec = WORKLOADS[args.workload]
     M = args.m or spec["M"]
     print(f"[bench] building {args.workload} ({args.layers} layers) on {torch.cuda.get_device_name(dev)}",
           file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
     stack = Stack(args.workload, args.layers, dev)
     print(f"[bench] weights resident after {stack.setup_s:.1f} s", file=sys.stderr, flush=True)
 
     def measure(m):
         io = stack.make_inputs(m)
         g = stack.capture(io)
-        ms = time_graph(torch, g, args.steps, args.warmup, dev)
+        ms, med, mn = time_graph(torch, g, args.steps, args.warmup, dev)
         nbytes = stack.pass_bytes(m)
-        print(f"[bench] M={m}: {ms:.4f} ms/pass, {nbytes / ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
-        return io, g, ms, nbytes
+        print(f"[bench] M={m}: {ms:.4f} ms/pass (median {med:.4f}, min {mn:.4f}), "
+              f"{nbytes / ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
+        return io, g, (ms, med, mn), nbytes
 
-    io, g, ms, nbytes = measure(M)
+    io, g, (ms, ms_med, ms_min), nbytes = measure(M)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    kmean_ms, kbytes, nlaunch = time_linear_launches(stack, io, max(1, min(args.steps, 5)))
+    kmean_ms, kbytes, nlaunch, kmed = time_linear_launches(stack, io, g, ms, max(1, min(args.steps, 5)))
     k_gbps = kbytes / (kmean_ms * 1e-3) / 1e9
+    print(f"[bench] linear launches: mean {kmean_ms * 1e3:.2f} us, {k_gbps:.1f} GB/s; per kind us {kmed}",
+          file=sys.stderr, flush=True)
+    traffic, traffic_src = profiled_traffic(args.workload, M)
     ops_per_pass = sum(2 * M * N * K for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
+    kops = ops_per_pass / (args.layers * len(LAYER_LAUNCHES))  # mean int ops per linear launch
     wbytes = sum(weight_bytes(N, K, stack.fmt, stack.group) for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
     out = {
         "metric": "W4A8 linear: achieved HBM GB/s and % of peak at M=1 and M=16 (verify)",
@@ -285,11 +361,14 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_median": round(ms_med, 5),
+        "ms_per_step_min": round(ms_min, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8" if stack.fmt == "w8" else "int8xint4",
         "data": "synthetic (seeded; weights drawn on the device, activations on the host)",
+        "kernel_digest": source_digest(),
         "config": {"workload": args.workload, "description": spec["desc"], "M": M,
                    "layers": args.layers, "weight_format": stack.fmt, "group": stack.group,
                    "bytes_per_pass": nbytes, "weight_bytes_per_pass": wbytes,
@@ -299,15 +378,20 @@ def main():
         "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1)},
         "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M),
                      "achieved": round(k_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(k_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": round(traffic) if traffic else None,
+                     "traffic_source": traffic_src,
                      "mean_launch_us": round(kmean_ms * 1e3, 3),
+                     "mean_launch_us_by_kind": kmed,
                      "mean_algorithmic_bytes_per_launch": round(kbytes),
                      "launches_timed": nlaunch,
-                     "int8_tops": round(ops_per_pass / (ms * 1e-3) / 1e12, 2)},
+                     "int8_tops_pass": round(ops_per_pass / (ms * 1e-3) / 1e12, 2),
+                     "int8_tops_kernel": round(kops / (kmean_ms * 1e-3) / 1e12, 2),
+                     "mfma_frac_kernel": round(kops / (kmean_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)},
     }
     if args.workload != "stack_w8" and M != 1 and not args.no_decode:
         del g
-        _io1, g1, ms1, nbytes1 = measure(1)
+        _io1, g1, (ms1, _med1, _min1), nbytes1 = measure(1)
         out["decode_m1"] = {"ms_per_pass": round(ms1, 5), "GB_per_s": round(nbytes1 / (ms1 * 1e-3) / 1e9, 2),
                             "frac_of_hbm_peak": round(nbytes1 / (ms1 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                             "bytes_per_pass": nbytes1}
@@ -316,7 +400,7 @@ def main():
     if args.sweep:
         rows = []
         for m in [int(v) for v in args.sweep.split(",")]:
-            _iom, gm, msm, nbm = measure(m)
+            _iom, gm, (msm, _medm, _minm), nbm = measure(m)
             rows.append({"M": m, "ms_per_pass": round(msm, 5), "GB_per_s": round(nbm / (msm * 1e-3) / 1e9, 2),
                          "bytes_per_pass": nbm})
             del gm

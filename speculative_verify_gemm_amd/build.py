@@ -34,6 +34,23 @@ CFLAGS = [
 ]
 
 
+def source_digest() -> str:
+    """Digest of everything that decides the built kernels: the sources, the
+    public header and the compile flags.  Profile summaries record it, so a
+    counter reading can be matched to the code it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "include", "svgemm.h"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(CFLAGS[:-4]).encode())  # flags, without the include paths
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):

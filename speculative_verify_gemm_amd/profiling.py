@@ -1,0 +1,199 @@
+"""Short text summaries of rocprofv3 runs of bench.py, for profiles/.
+
+    python -m speculative_verify_gemm_amd.profiling trace <trace dir> --cmd "<command>" --out <file.md>
+    python -m speculative_verify_gemm_amd.profiling traffic <fetch dir> <write dir> --calib-mib 256 \\
+        --workload stack_w4g64 --m 16 --fetch-json <bench out> --write-json <bench out> \\
+        --cmd "<commands>" --out <file.md>
+
+`trace` reads the kernel trace (`--kernel-trace`, csv) and lists every kernel's
+dispatch count and mean / median / min duration, with the W4A8 and W8A8 linear
+kernels also pooled over the launch mix of a pass.
+
+`traffic` reads two counter runs (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`):
+each counter is scaled by what it reads for the device-to-device copy of
+`--calib-mib` MiB that bench.py makes first (`--calib-copy-mib`), whose true
+size is known, and the linear kernels' HBM bytes per launch are pooled the same
+way.  The summary records the digest of the kernel sources the runs were taken
+on (which bench.py prints in its JSON line); bench.py reports the figure only
+while that digest still matches the sources.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _rows(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    out = []
+    for f in files:
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _short(name):
+    """Kernel name without the argument list and anonymous-namespace noise."""
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth = 0
+    for i, c in enumerate(n):
+        depth += c == "<"
+        depth -= c == ">"
+        if c == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def _is_linear(name):
+    return name.startswith("k_linear<")
+
+
+def _policy(name):
+    """'k_linear<MfmaW4<1, 64, false, false>, 8, 4, 4>' -> 'MfmaW4<1, 64, false, false>'."""
+    inner = name[len("k_linear<"):]
+    depth = 0
+    for i, c in enumerate(inner):
+        depth += c == "<"
+        depth -= c == ">"
+        if c == "," and depth == 0:
+            return inner[:i]
+    return inner
+
+
+def trace_summary(d, cmd):
+    rows = _rows(d, "kernel_trace.csv")
+    by, other = {}, []
+    for r in rows:
+        n = _short(r["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if not n.startswith("k_"):
+            other.append(dur)
+            continue
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        by.setdefault((n, wgs, int(r["Workgroup_Size_X"])), []).append(dur)
+    lines = ["# rocprofv3 kernel trace", "", "Command:", "", "```", cmd, "```", "",
+             "Durations are kernel-trace spans (start to end of each dispatch).", "",
+             "| kernel | workgroups x threads | dispatches | mean us | median us | min us |",
+             "|---|---|---|---|---|---|"]
+    for (n, wgs, wg), v in sorted(by.items()):
+        lines.append(f"| `{n}` | {wgs} x {wg} | {len(v)} | {statistics.mean(v):.2f} | "
+                     f"{statistics.median(v):.2f} | {min(v):.2f} |")
+    pooled = {}
+    for (n, _w, _g), v in by.items():
+        if _is_linear(n):
+            pooled.setdefault(_policy(n), []).extend(v)
+    if pooled:
+        lines += ["", "Linear kernels pooled per policy over all launch shapes of a pass:", ""]
+        for pol, v in sorted(pooled.items()):
+            lines.append(f"- `{pol}`: {len(v)} dispatches, mean {statistics.mean(v):.3f} us, "
+                         f"median {statistics.median(v):.3f} us")
+    if other:
+        lines += ["", f"Other kernels (torch weight generation and fills at set-up): {len(other)} dispatches, "
+                      f"{sum(other) / 1e3:.1f} ms in total."]
+    return "\n".join(lines) + "\n"
+
+
+def _counter(rows, counter):
+    """{dispatch id: (kernel, value)} for one counter (KiB per dispatch)."""
+    out = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        did = r["Dispatch_Id"]
+        k, v = out.get(did, (r["Kernel_Name"], 0.0))
+        out[did] = (k, v + float(r["Counter_Value"]))
+    return out
+
+
+def _scale(vals, calib_kib):
+    """Factor that maps the counter onto true KiB, from the calibration copy:
+    the copy dispatches reading at least half of its size."""
+    copies = [v for k, v in vals.values() if COPY_KERNEL in k and v >= 0.5 * calib_kib]
+    if not copies:
+        raise SystemExit("no calibration copy found in the counter run")
+    return calib_kib / statistics.median(copies), len(copies)
+
+
+def _run_digest(bench_json):
+    """The kernel digest bench.py printed in a profiled run."""
+    import json
+    with open(bench_json) as f:
+        lines = [ln for ln in f if ln.startswith("{")]
+    if not lines:
+        raise SystemExit(f"no bench JSON line in {bench_json}")
+    return json.loads(lines[-1])["kernel_digest"]
+
+
+def traffic_summary(fetch_dir, write_dir, calib_mib, workload, M, cmd, fetch_json, write_json):
+    digest = _run_digest(fetch_json)
+    if _run_digest(write_json) != digest:
+        raise SystemExit("the two counter runs were taken on different kernels")
+    calib_kib = calib_mib * 1024.0
+    fetch = _counter(_rows(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = _counter(_rows(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    ff, nf = _scale(fetch, calib_kib)
+    fw, nw = _scale(write, calib_kib)
+    lf = [v for k, v in fetch.values() if _is_linear(_short(k))]
+    lw = [v for k, v in write.values() if _is_linear(_short(k))]
+    if not lf or not lw:
+        raise SystemExit("no linear kernel dispatch in the counter runs")
+    fetch_b = statistics.mean(lf) * ff * 1024.0
+    write_b = statistics.mean(lw) * fw * 1024.0
+    lines = ["# rocprofv3 HBM traffic of the linear kernels", "", "Commands (two counter runs):", "", "```",
+             cmd, "```", "",
+             f"workload: {workload} M={M}",
+             f"digest: {digest}",
+             f"calibration: device-to-device copy of {calib_mib} MiB; FETCH_SIZE scale {ff:.4f} "
+             f"({nf} copies), WRITE_SIZE scale {fw:.4f} ({nw} copies)",
+             f"linear dispatches counted: {len(lf)} (fetch run), {len(lw)} (write run)",
+             f"fetch_bytes_per_launch: {fetch_b:.6g}",
+             f"write_bytes_per_launch: {write_b:.6g}",
+             f"traffic_bytes_per_launch: {fetch_b + write_b:.6g}", ""]
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description="summarize rocprofv3 runs of bench.py")
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out", required=True)
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_dir")
+    c.add_argument("write_dir")
+    c.add_argument("--calib-mib", type=int, required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--m", type=int, required=True)
+    c.add_argument("--fetch-json", required=True, help="bench.py output of the FETCH_SIZE run")
+    c.add_argument("--write-json", required=True, help="bench.py output of the WRITE_SIZE run")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "trace":
+        text = trace_summary(a.dir, a.cmd)
+    else:
+        text = traffic_summary(a.fetch_dir, a.write_dir, a.calib_mib, a.workload, a.m, a.cmd,
+                               a.fetch_json, a.write_json)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
