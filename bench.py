@@ -3,9 +3,12 @@
 
 A step is one pass over a ~7B-parameter synthetic projection stack (32 layers
 of q/k/v/o 4096x4096, gate/up 4096->12288, down 12288->4096): for each layer
-and each of its four input spaces, the activation rows are rotated and
-quantized (act_rht_quant_i8), then the linear(s) consuming them run (q/k/v
-stacked along N into one launch, gate/up into one).  Weights are rotated and
+and each of its four input spaces, the fp32 activation rows are rotated and
+quantized, and the linear(s) consuming them run (q/k/v stacked along N into
+one launch, gate/up into one).  By default each such step goes through
+act_quant_w4a8_linear / act_quant_w8a8_linear, which is ONE launch for
+M <= 2 (every workgroup quantizes the rows itself) and two otherwise;
+--unfused always runs act_rht_quant_i8 and the linear as two launches.  Weights are rotated and
 quantized once at setup (rht_rotate_weights) and stay resident in HBM.  The
 pass is captured in a HIP graph and replayed.
 
@@ -76,11 +79,12 @@ def weight_bytes(N, K, fmt, group):
 class Stack:
     """The synthetic stack resident on the device, and its captured passes."""
 
-    def __init__(self, workload, layers, dev):
+    def __init__(self, workload, layers, dev, fused=True):
         import torch
         import speculative_verify_gemm_amd as svg
         import synth
         self.torch, self.svg, self.synth = torch, svg, synth
+        self.fused = fused
         self.wl = workload
         self.spec = WORKLOADS[workload]
         self.fmt, self.group = self.spec["fmt"], self.spec["group"]
@@ -125,19 +129,32 @@ class Stack:
         return dict(M=M, xin=xin, xq=dict(zip([s for s, _ in synth.STACK_SPACES], xq)),
                     xs=dict(zip([s for s, _ in synth.STACK_SPACES], xs)), ys=ys)
 
-    def linear(self, io, L, name, space):
+    def linear(self, io, L, name, space, fused=None):
         wq, ws, wz, N = self.w[L][name]
+        if self.fused if fused is None else fused:
+            X, sg = io["xin"][L][space], self.signs[L][space]
+            xq, xs, y = io["xq"][space], io["xs"][space], io["ys"][L][name]
+            if self.fmt == "w8":
+                self.svg.act_quant_w8a8_linear(X, sg, xq, xs, wq, ws, N, y)
+            else:
+                self.svg.act_quant_w4a8_linear(X, sg, xq, xs, wq, ws, wz, self.fmt, self.group, N, y)
+            return
         if self.fmt == "w8":
             self.svg.w8a8_linear(io["xq"][space], io["xs"][space], wq, ws, N, io["ys"][L][name])
         else:
             self.svg.w4a8_linear(io["xq"][space], io["xs"][space], wq, ws, wz, self.fmt, self.group,
                                  N, io["ys"][L][name])
 
+    def quantize(self, io, L, space, force=False):
+        """The separate activation step of the unfused pass (nothing when fused)."""
+        if force or not self.fused:
+            self.svg.act_rht_quant_i8(io["xin"][L][space], self.signs[L][space], io["xq"][space],
+                                      io["xs"][space])
+
     def run_pass(self, io, events=None):
-        svg = self.svg
         for L in range(self.layers):
             for name, _members, _N, _K, space in LAYER_LAUNCHES:
-                svg.act_rht_quant_i8(io["xin"][L][space], self.signs[L][space], io["xq"][space], io["xs"][space])
+                self.quantize(io, L, space)
                 if events is not None:
                     e0, e1 = events.pop()
                     e0.record()
@@ -182,16 +199,20 @@ def time_graph(torch, g, steps, warmup, dev):
 
 
 def time_linear_launches(stack, io, g, ms_graph, steps):
-    """Mean duration of the linear launches, from HIP events recorded on the
-    stream they run on.  For each launch kind of a layer (qkv, o, gate/up,
-    down) the launches of all layers run back to back between two events (the
-    activations quantized once before, untimed), so the event overhead spreads
-    over `layers` launches and each launch counts from the end of the previous
-    one to its own end -- the same span a kernel trace reports.  Before each
-    step the captured pass is replayed enough times to keep the device busy
-    while the host enqueues, so no host launch latency enters the timed spans.
+    """Mean duration of the linear kernel's launches, from HIP events recorded
+    on the stream they run on.  For each launch kind of a layer (qkv, o,
+    gate/up, down) the launches of all layers run back to back between two
+    events, so the event overhead spreads over `layers` launches and each
+    launch counts from the end of the previous one to its own end -- the span
+    a kernel trace reports.  The kernel timed is the one that does the
+    contraction: the fused kernel (which also quantizes its input) where the
+    pass fuses (M <= 2), else the linear alone on activations quantized once
+    before, untimed.  Before each step the captured pass is replayed enough
+    times to keep the device busy while the host enqueues, so no host launch
+    latency enters the timed spans.
     Returns (mean ms, mean algorithmic bytes, launches, {kind: mean us})."""
     torch = stack.torch
+    fused = stack.fused and io["M"] <= 2
     t0 = time.perf_counter()
     stack.run_pass(io)                       # host cost of enqueuing one eager pass
     enqueue_ms = (time.perf_counter() - t0) * 1e3
@@ -203,12 +224,12 @@ def time_linear_launches(stack, io, g, ms_graph, steps):
             g.replay()
         spans = []
         for name, _m, _N, _K, space in LAYER_LAUNCHES:
-            stack.svg.act_rht_quant_i8(io["xin"][0][space], stack.signs[0][space], io["xq"][space],
-                                       io["xs"][space])
+            if not fused:
+                stack.quantize(io, 0, space, force=True)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for L in range(stack.layers):
-                stack.linear(io, L, name, space)
+                stack.linear(io, L, name, space, fused=fused)
             e1.record()
             spans.append((name, e0, e1))
         torch.cuda.synchronize(stack.dev)
@@ -221,9 +242,10 @@ def time_linear_launches(stack, io, g, ms_graph, steps):
             {n: round(v * 1e3, 3) for n, v in mean_kind.items()})
 
 
-def kernel_name(fmt, group, M):
+def kernel_name(fmt, group, M, fused):
     """The linear kernel template instance a launch of this format and M runs
-    (k_linear<policy, waves, chunks per wave, batch>; the shape varies with K)."""
+    (k_linear[_fused]<policy, waves, chunks per wave, batch>; the shape varies
+    with K)."""
     if fmt == "w8":
         pol = f"DotW8<{M}>" if M <= 2 else f"MfmaW8<{1 if M <= 16 else 2}>"
     else:
@@ -232,7 +254,7 @@ def kernel_name(fmt, group, M):
             pol = f"DotW4<{1 if M <= 1 else 2 if M <= 2 else 8}, {group}, {z4}, false>"
         else:
             pol = f"MfmaW4<{1 if M <= 16 else 2}, {group}, {z4}, false>"
-    return f"k_linear<{pol}, ...>"
+    return f"k_linear{'_fused' if fused and M <= 2 else ''}<{pol}, ...>"
 
 
 def profiled_traffic(workload, M):
@@ -304,6 +326,8 @@ def main():
     ap.add_argument("--workload", default="stack_w4g64", choices=sorted(WORKLOADS))
     ap.add_argument("--m", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--unfused", action="store_true",
+                    help="quantize activations in a launch of their own before each linear")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the M=1 comparison pass")
     ap.add_argument("--sweep", default=None, help="comma-separated M values: report a pass per M")
@@ -331,7 +355,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize(dev)
         del src, dst
-    stack = Stack(args.workload, args.layers, dev)
+    stack = Stack(args.workload, args.layers, dev, fused=not args.unfused)
     print(f"[bench] weights resident after {stack.setup_s:.1f} s", file=sys.stderr, flush=True)
 
     def measure(m):
@@ -372,11 +396,12 @@ def main():
         "config": {"workload": args.workload, "description": spec["desc"], "M": M,
                    "layers": args.layers, "weight_format": stack.fmt, "group": stack.group,
                    "bytes_per_pass": nbytes, "weight_bytes_per_pass": wbytes,
-                   "launches_per_pass": args.layers * len(LAYER_LAUNCHES) * 2},
+                   "launches_per_pass": args.layers * len(LAYER_LAUNCHES) * (1 if stack.fused and M <= 2 else 2),
+                   "fused_activation_quantization": stack.fused and M <= 2},
         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "passes_per_s": round(1e3 / ms, 2),
         "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1)},
-        "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M),
+        "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M, stack.fused),
                      "achieved": round(k_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic else None,

@@ -184,6 +184,33 @@ svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
                        const int8_t* wq, const uint16_t* w_scale, int N, float* y,
                        int32_t* partials_debug, void* stream);
 
+/*
+ * act_quant_w4a8_linear, act_quant_w8a8_linear -- act_rht_quant_i8 followed by
+ * w4a8_linear / w8a8_linear, taking the fp32 activation rows directly.
+ * [KT "How Uzu optimizes bytes and tokens per pass": activations quantized on
+ *  the fly; "Why batch-one decoding is memory-bound": a decode pass is the
+ *  weight stream, so the activation step should not cost a launch of its own.]
+ *
+ *  X, signs, block   as for act_rht_quant_i8.
+ *  xq, x_scale       OUTPUTS here (as from act_rht_quant_i8), then read by the
+ *                    contraction; the results are bit-identical to the two
+ *                    separate calls.
+ *  wq ... partials_debug   as for w4a8_linear / w8a8_linear.
+ *
+ *  For M <= 2 and K <= 12288 this is ONE launch: every workgroup quantizes the
+ *  rows itself while its first weights are in flight.  Otherwise it enqueues
+ *  the two launches.  Errors as for the two separate calls; N == 0 runs the
+ *  quantization alone.
+ */
+svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
+                                 int8_t* xq, float* x_scale, const uint8_t* wq,
+                                 const uint16_t* w_scale, const void* w_zero, int fmt, int group,
+                                 int N, float* y, int32_t* partials_debug, void* stream);
+svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
+                                 int8_t* xq, float* x_scale, const int8_t* wq,
+                                 const uint16_t* w_scale, int N, float* y,
+                                 int32_t* partials_debug, void* stream);
+
 /* Text of the last error on the calling thread ("" after a successful call);
  * valid until the next call on this thread. */
 const char* svg_last_error(void);

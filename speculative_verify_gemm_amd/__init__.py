@@ -41,7 +41,10 @@ def _load():
     lib.act_rht_quant_i8.argtypes = [vp, i, i, vp, i, vp, vp, vp]
     lib.w4a8_linear.argtypes = [vp, vp, i, i, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.w8a8_linear.argtypes = [vp, vp, i, i, vp, vp, i, vp, vp, vp]
-    for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear):
+    lib.act_quant_w4a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.act_quant_w8a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, i, vp, vp, vp]
+    for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear,
+               lib.act_quant_w4a8_linear, lib.act_quant_w8a8_linear):
         fn.restype = ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.svg_weight_sizes.argtypes = [i, i, i, i, u64p, u64p, u64p]
@@ -181,7 +184,56 @@ def w8a8_linear(xq, x_scale, wq, w_scale, N, y, partials_debug=None, stream=None
                            _p(partials_debug), _stream(stream, xq)))
 
 
+def _check_fused(X, signs, xq, x_scale):
+    _dev(X, "X", torch.float32)
+    _dev(signs, "signs", torch.int8)
+    if tuple(xq.shape) != tuple(X.shape):
+        raise ValueError("xq must have the shape of X")
+
+
+def act_quant_w4a8_linear(X, signs, xq, x_scale, wq, w_scale, w_zero, fmt, group, N, y,
+                          partials_debug=None, block=BLOCK, stream=None):
+    """act_rht_quant_i8 then w4a8_linear (one launch for M <= 2): fp32 X[M, K]
+    in, xq / x_scale (written) and y[M, N] out."""
+    _check_fused(X, signs, xq, x_scale)
+    f = _fmt(fmt)
+    _dev(xq, "xq", torch.int8)
+    _dev(x_scale, "x_scale", torch.float32)
+    _dev(y, "y", torch.float32)
+    M, K = X.shape
+    _check_storage(N, K, f, group, wq, w_scale, w_zero)
+    if tuple(y.shape) != (M, N) or tuple(x_scale.shape) != (M,):
+        raise ValueError("y must be [M, N] and x_scale [M]")
+    if partials_debug is not None:
+        _dev(partials_debug, "partials_debug", torch.int32)
+        if tuple(partials_debug.shape) != (M, N, K // group):
+            raise ValueError("partials_debug must be [M, N, K/g]")
+    _check(lib.act_quant_w4a8_linear(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale), _p(wq),
+                                     _p(w_scale), _p(w_zero), f, group, N, _p(y), _p(partials_debug),
+                                     _stream(stream, X)))
+
+
+def act_quant_w8a8_linear(X, signs, xq, x_scale, wq, w_scale, N, y, partials_debug=None,
+                          block=BLOCK, stream=None):
+    """act_rht_quant_i8 then w8a8_linear (one launch for M <= 2)."""
+    _check_fused(X, signs, xq, x_scale)
+    _dev(xq, "xq", torch.int8)
+    _dev(x_scale, "x_scale", torch.float32)
+    _dev(y, "y", torch.float32)
+    M, K = X.shape
+    _check_storage(N, K, W8, 0, wq, w_scale, None)
+    if tuple(y.shape) != (M, N) or tuple(x_scale.shape) != (M,):
+        raise ValueError("y must be [M, N] and x_scale [M]")
+    if partials_debug is not None:
+        _dev(partials_debug, "partials_debug", torch.int32)
+        if tuple(partials_debug.shape) != (M, N):
+            raise ValueError("partials_debug must be [M, N]")
+    _check(lib.act_quant_w8a8_linear(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale), _p(wq),
+                                     _p(w_scale), N, _p(y), _p(partials_debug), _stream(stream, X)))
+
+
 # ------------------------------------------------------------- allocation
+
 def empty_weights(N, K, fmt, group, device="cuda"):
     """Uninitialised tiled storage for rht_rotate_weights: flat (wq, w_scale,
     w_zero) tensors (w_zero is None for W8)."""

@@ -111,6 +111,8 @@ struct W4Common {
   float* y;
   int32_t* dbg;
   float* red;
+  const int8_t* xlds = nullptr;  // LDS copy of the quantized rows (fused GEMV), row stride xlds_row
+  int xlds_row = 0;
 
   template <int G, bool Z4>
   SVG_DEV void setup(const LinArgs& a, float* red_) {
@@ -153,7 +155,7 @@ struct W4Common {
 template <int MH, int G, bool Z4, bool DBG>
 struct MfmaW4 : W4Common {
   static_assert(G == 64 || G == 128, "MFMA path handles groups of 64 and 128");
-  static constexpr int kChunkK = 128, kActRegs = 8 * MH, kRedRows = MH * 16;
+  static constexpr int kChunkK = 128, kActRegs = 8 * MH, kRedRows = MH * 16, kMaxTok = 16 * MH;
   static constexpr int kBatchRegs = 6, kFixedRegs = 48;
   static constexpr int GPC = 128 / G;  // groups per 128-k chunk
   using red_t = float;
@@ -177,8 +179,9 @@ struct MfmaW4 : W4Common {
       for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
   }
 
-  template <int NC>
+  template <int NC, bool LDS = false>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
+    static_assert(!LDS, "the MFMA policy reads its activation rows from global memory");
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -273,7 +276,7 @@ struct MfmaW4 : W4Common {
 // gives it.
 template <int MT, int G, bool Z4, bool DBG>
 struct DotW4 : W4Common {
-  static constexpr int kChunkK = 128, kActRegs = 8 * MT, kRedRows = MT;
+  static constexpr int kChunkK = 128, kActRegs = 8 * MT, kRedRows = MT, kMaxTok = MT;
   static constexpr int kBatchRegs = 6, kFixedRegs = 48;
   static constexpr int GPC = 128 / G;
   using red_t = float;
@@ -298,15 +301,23 @@ struct DotW4 : W4Common {
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
   }
 
-  template <int NC>
+  template <int NC, bool LDS = false>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const u32 xo = x_off(m, j0 + c);
-        X.a1[c][m] = bload16(xr, xo);
-        X.a2[c][m] = bload16(xr, xo + 64u);
+        if constexpr (LDS) {  // rows past M and k past K are zero in the copy
+          const int j = j0 + c;
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          const int8_t* row = xlds + m * xlds_row + j * 128 + 16 * b;
+          X.a1[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(row) : zero;
+          X.a2[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(row + 64) : zero;
+        } else {
+          const u32 xo = x_off(m, j0 + c);
+          X.a1[c][m] = bload16(xr, xo);
+          X.a2[c][m] = bload16(xr, xo + 64u);
+        }
       }
   }
 
@@ -399,11 +410,17 @@ struct DotW4 : W4Common {
 
 // --------------------------------------------------------------- dispatch
 template <int G, bool Z4, bool DBG>
-hipError_t dispatch_g(const LinArgs& a, hipStream_t stream) {
-  if (a.M <= 1) return launch_linear_auto<DotW4<1, G, Z4, DBG>>(a, stream);
-  if (a.M <= kGemvMaxM) return launch_linear_auto<DotW4<2, G, Z4, DBG>>(a, stream);
+hipError_t dispatch_g(const LinArgs& a, const ActIn* f, hipStream_t stream) {
+  if (a.M <= 1) return launch_linear_auto<DotW4<1, G, Z4, DBG>>(a, f, stream);
+  if (a.M <= kGemvMaxM) return launch_linear_auto<DotW4<2, G, Z4, DBG>>(a, f, stream);
   if constexpr (G == 32) {
-    // no MFMA form for 32-wide groups: the dot kernel, 8 tokens per launch
+    // no MFMA form for 32-wide groups: the dot kernel, 8 tokens per launch,
+    // after a separate quantization of all rows when the input is fp32
+    if (f) {
+      hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, const_cast<int8_t*>(a.xq),
+                                              const_cast<float*>(a.x_scale), stream);
+      if (e != hipSuccess) return e;
+    }
     const int NG = a.K / G;
     for (int m0 = 0; m0 < a.M; m0 += 8) {
       LinArgs s = a;
@@ -412,13 +429,13 @@ hipError_t dispatch_g(const LinArgs& a, hipStream_t stream) {
       s.x_scale = a.x_scale + m0;
       s.y = a.y + (size_t)m0 * a.N;
       s.dbg = DBG ? a.dbg + (size_t)m0 * a.N * NG : nullptr;
-      hipError_t e = launch_linear_auto<DotW4<8, G, Z4, DBG>>(s, stream);
+      hipError_t e = launch_linear_auto<DotW4<8, G, Z4, DBG>>(s, nullptr, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   } else {
-    if (a.M <= 16) return launch_linear_auto<MfmaW4<1, G, Z4, DBG>>(a, stream);
-    return launch_linear_auto<MfmaW4<2, G, Z4, DBG>>(a, stream);
+    if (a.M <= 16) return launch_linear_auto<MfmaW4<1, G, Z4, DBG>>(a, f, stream);
+    return launch_linear_auto<MfmaW4<2, G, Z4, DBG>>(a, f, stream);
   }
 }
 
@@ -426,12 +443,15 @@ hipError_t dispatch_g(const LinArgs& a, hipStream_t stream) {
 
 hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
-                           float* y, int32_t* dbg, hipStream_t stream) {
+                           float* y, int32_t* dbg, const float* X, const int8_t* signs,
+                           hipStream_t stream) {
   const LinArgs a{xq, x_scale, M, K, wq, w_scale, w_zero, N, y, dbg};
-#define SVG_G_CASE(G)                                                                          \
-  if (group == G) {                                                                            \
-    if (dbg) return z4 ? dispatch_g<G, true, true>(a, stream) : dispatch_g<G, false, true>(a, stream); \
-    return z4 ? dispatch_g<G, true, false>(a, stream) : dispatch_g<G, false, false>(a, stream);  \
+  const ActIn fa{X, signs};
+  const ActIn* f = X ? &fa : nullptr;
+#define SVG_G_CASE(G)                                                                                  \
+  if (group == G) {                                                                                    \
+    if (dbg) return z4 ? dispatch_g<G, true, true>(a, f, stream) : dispatch_g<G, false, true>(a, f, stream); \
+    return z4 ? dispatch_g<G, true, false>(a, f, stream) : dispatch_g<G, false, false>(a, f, stream);  \
   }
   SVG_G_CASE(32)
   SVG_G_CASE(64)

@@ -38,6 +38,8 @@ struct W8Common {
   float* y;
   int32_t* dbg;
   int* red;
+  const int8_t* xlds = nullptr;  // LDS copy of the quantized rows (fused GEMV), row stride xlds_row
+  int xlds_row = 0;
 
   SVG_DEV void setup(const LinArgs& a, int* red_) {
     const int ntiles = (a.N + kTileRows - 1) / kTileRows;
@@ -77,7 +79,7 @@ struct W8Common {
 
 template <int MT>
 struct DotW8 : W8Common {
-  static constexpr int kChunkK = 64, kActRegs = 4 * MT, kRedRows = MT;
+  static constexpr int kChunkK = 64, kActRegs = 4 * MT, kRedRows = MT, kMaxTok = MT;
   static constexpr int kBatchRegs = 4, kFixedRegs = 36;
   using red_t = int;
   template <int NC>
@@ -96,12 +98,20 @@ struct DotW8 : W8Common {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0;
   }
-  template <int NC>
+  template <int NC, bool LDS = false>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) X.a[c][m] = bload16(xr, x_off(m, j0 + c));
+      for (int m = 0; m < MT; ++m) {
+        if constexpr (LDS) {  // rows past M and k past K are zero in the copy
+          const int j = j0 + c;
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          X.a[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(xlds + m * xlds_row + j * 64 + 16 * b) : zero;
+        } else {
+          X.a[c][m] = bload16(xr, x_off(m, j0 + c));
+        }
+      }
   }
   template <int U>
   SVG_DEV void load(Batch<U>& B, int t, int j0, bool valid) const {
@@ -141,7 +151,7 @@ struct DotW8 : W8Common {
 
 template <int MH>
 struct MfmaW8 : W8Common {
-  static constexpr int kChunkK = 64, kActRegs = 4 * MH, kRedRows = MH * 16;
+  static constexpr int kChunkK = 64, kActRegs = 4 * MH, kRedRows = MH * 16, kMaxTok = 16 * MH;
   static constexpr int kBatchRegs = 4, kFixedRegs = 36;
   using red_t = int;
   template <int NC>
@@ -160,8 +170,9 @@ struct MfmaW8 : W8Common {
 #pragma unroll
     for (int h = 0; h < MH; ++h) acc[h] = v4i{0, 0, 0, 0};
   }
-  template <int NC>
+  template <int NC, bool LDS = false>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
+    static_assert(!LDS, "the MFMA policy reads its activation rows from global memory");
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -202,11 +213,13 @@ struct MfmaW8 : W8Common {
 }  // namespace
 
 hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
-                           const uint16_t* w_scale, int N, float* y, int32_t* dbg,
-                           hipStream_t stream) {
+                           const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
+                           const int8_t* signs, hipStream_t stream) {
   const LinArgs a{xq, x_scale, M, K, wq, w_scale, nullptr, N, y, dbg};
-  if (M <= 1) return launch_linear_auto<DotW8<1>>(a, stream);
-  if (M <= kGemvMaxM) return launch_linear_auto<DotW8<2>>(a, stream);
-  if (M <= 16) return launch_linear_auto<MfmaW8<1>>(a, stream);
-  return launch_linear_auto<MfmaW8<2>>(a, stream);
+  const ActIn fa{X, signs};
+  const ActIn* f = X ? &fa : nullptr;
+  if (M <= 1) return launch_linear_auto<DotW8<1>>(a, f, stream);
+  if (M <= kGemvMaxM) return launch_linear_auto<DotW8<2>>(a, f, stream);
+  if (M <= 16) return launch_linear_auto<MfmaW8<1>>(a, f, stream);
+  return launch_linear_auto<MfmaW8<2>>(a, f, stream);
 }

@@ -1,7 +1,8 @@
 // Block-diagonal random Hadamard transform fused with quantization, gfx950.
 //
 //  * k_act_rht_quant   -- activations: sign flip + 32-wide butterfly, per-row
-//                         |u| max, int8 codes and the per-row scale.
+//                         |u| max, int8 codes and the per-row scale (one
+//                         workgroup per token row, svg_act.h).
 //  * k_rot_quant_w4    -- weights, 4-bit asymmetric per group along K.
 //  * k_rot_quant_w8    -- weights, 8-bit symmetric per row.
 //
@@ -12,17 +13,18 @@
 // activations are quantized to 8 bits on the fly, Medium weights are 4-bit
 // asymmetric and Large weights 8-bit symmetric.
 //
-// Mapping: a 256-thread workgroup owns one row.  Each thread holds one float4
-// (4 consecutive values), so a 32-block spans 8 consecutive lanes and the
+// Mapping: a workgroup owns one row.  Each thread holds float4 chunks (4
+// consecutive values), so a 32-block spans 8 consecutive lanes and the
 // butterfly needs only lane exchanges (DPP and ds_swizzle), no LDS traffic.
-// Row-wide maxima use two passes over the row (the second pass recomputes the
-// transform from the L2-resident input, which is bit-identical), so any K is
-// handled without holding the row in registers.
+// The weight kernels take row-wide maxima in two passes over the row (the
+// second pass recomputes the transform from the L2-resident input, which is
+// bit-identical), so any K is handled without holding the row in registers.
 //
 // Everything that decides an integer code is one IEEE fp32 operation with
 // round-to-nearest-even (this file is compiled with -ffp-contract=off and
 // correctly rounded division): the codes match a plain fp32 implementation of
 // the same steps bit for bit.
+#include "svg_act.h"
 #include "svg_device.h"
 #include "svg_internal.h"
 
@@ -59,97 +61,15 @@ SVG_DEV float block_max(float v, float* red) {
   return r;
 }
 
-SVG_DEV int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-
 #pragma clang fp contract(off)
 
-__global__ __launch_bounds__(kThreads) void k_act_rht_quant(const float* __restrict__ X, int K,
-                                                           const int8_t* __restrict__ signs,
-                                                           int8_t* __restrict__ xq,
-                                                           float* __restrict__ x_scale) {
-  __shared__ float red[kThreads / 64];
+template <int NT, int CPT>
+__global__ __launch_bounds__(NT) void k_act_rht_quant(const float* __restrict__ X, int K,
+                                                     const int8_t* __restrict__ signs,
+                                                     int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+  __shared__ float red[16];
   const int m = blockIdx.x;
-  const float* row = X + (size_t)m * K;
-  const int nchunk = K >> 2;
-  float amax = 0.f;
-  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
-    const int c = c0 + threadIdx.x;
-    const bool valid = c < nchunk;
-    float e0, e1, e2, e3;
-    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
-    if (valid) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0), fabsf(e1)), fmaxf(fabsf(e2), fabsf(e3))));
-  }
-  amax = block_max(amax, red);
-  const float sigma = amax / 127.0f;
-  if (threadIdx.x == 0) x_scale[m] = sigma * 0.03125f;  // exact: carries the transform's 2^-5
-  int8_t* out = xq + (size_t)m * K;
-  for (int c0 = 0; c0 < nchunk; c0 += kThreads) {
-    const int c = c0 + threadIdx.x;
-    const bool valid = c < nchunk;
-    float e0, e1, e2, e3;
-    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
-    if (valid) {
-      int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-      if (amax > 0.f) {
-        q0 = clamp_i((int)rintf(e0 / sigma), -127, 127);
-        q1 = clamp_i((int)rintf(e1 / sigma), -127, 127);
-        q2 = clamp_i((int)rintf(e2 / sigma), -127, 127);
-        q3 = clamp_i((int)rintf(e3 / sigma), -127, 127);
-      }
-      const u32 packed = (u32)(q0 & 0xFF) | ((u32)(q1 & 0xFF) << 8) | ((u32)(q2 & 0xFF) << 16) |
-                         ((u32)(q3 & 0xFF) << 24);
-      *reinterpret_cast<u32*>(out + 4 * c) = packed;
-    }
-  }
-}
-
-// Single-pass variant for K <= 4 * kThreads * CPT: every load of the row is
-// issued at once through buffer loads (zeros past K), the rotated values stay
-// in registers between the max reduction and the quantization.
-template <int CPT>
-__global__ __launch_bounds__(kThreads) void k_act_rht_quant_reg(const float* __restrict__ X, int K,
-                                                               const int8_t* __restrict__ signs,
-                                                               int8_t* __restrict__ xq,
-                                                               float* __restrict__ x_scale) {
-  __shared__ float red[kThreads / 64];
-  const int m = blockIdx.x;
-  const int nchunk = K >> 2;
-  const rsrc_t xr = make_rsrc(X + (size_t)m * K, (u32)K * 4u);
-  const rsrc_t sr = make_rsrc(signs, (u32)K);
-  float e[CPT][4];
-  int sg[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const u32 c = threadIdx.x + kThreads * i;
-    const u32x4 v = bload16(xr, c * 16u);
-    sg[i] = (int)bload4(sr, c * 4u);
-    e[i][0] = __uint_as_float(v[0]); e[i][1] = __uint_as_float(v[1]);
-    e[i][2] = __uint_as_float(v[2]); e[i][3] = __uint_as_float(v[3]);
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    apply_signs4(e[i][0], e[i][1], e[i][2], e[i][3], sg[i]);
-    fwht32_lane4(e[i][0], e[i][1], e[i][2], e[i][3]);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e[i][0]), fabsf(e[i][1])), fmaxf(fabsf(e[i][2]), fabsf(e[i][3]))));
-  }
-  amax = block_max(amax, red);
-  const float sigma = amax / 127.0f;
-  if (threadIdx.x == 0) x_scale[m] = sigma * 0.03125f;  // exact: carries the transform's 2^-5
-  int8_t* out = xq + (size_t)m * K;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    if (c < nchunk) {
-      int q[4] = {0, 0, 0, 0};
-      if (amax > 0.f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) q[t] = clamp_i((int)rintf(e[i][t] / sigma), -127, 127);
-      }
-      *reinterpret_cast<u32*>(out + 4 * c) = (u32)(q[0] & 0xFF) | ((u32)(q[1] & 0xFF) << 8) |
-                                             ((u32)(q[2] & 0xFF) << 16) | ((u32)(q[3] & 0xFF) << 24);
-    }
-  }
+  act_quant_row<CPT>(X + (size_t)m * K, K, signs, StoreGlobal<0>(xq + (size_t)m * K, x_scale + m, K), red);
 }
 
 // Group-wise min/max over the LPG = G/4 lanes that hold one quantization group.
@@ -314,20 +234,17 @@ __global__ __launch_bounds__(kThreads) void k_fill_zero(u32* __restrict__ p, siz
 
 hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int8_t* xq,
                                     float* x_scale, hipStream_t stream) {
-  const int cpt = (K / 4 + kThreads - 1) / kThreads;  // float4 chunks per thread
-  const dim3 grid(M), block(kThreads);
-  if (cpt <= 1)
-    hipLaunchKernelGGL((k_act_rht_quant_reg<1>), grid, block, 0, stream, X, K, signs, xq, x_scale);
-  else if (cpt <= 2)
-    hipLaunchKernelGGL((k_act_rht_quant_reg<2>), grid, block, 0, stream, X, K, signs, xq, x_scale);
-  else if (cpt <= 4)
-    hipLaunchKernelGGL((k_act_rht_quant_reg<4>), grid, block, 0, stream, X, K, signs, xq, x_scale);
-  else if (cpt <= 8)
-    hipLaunchKernelGGL((k_act_rht_quant_reg<8>), grid, block, 0, stream, X, K, signs, xq, x_scale);
-  else if (cpt <= 16)
-    hipLaunchKernelGGL((k_act_rht_quant_reg<16>), grid, block, 0, stream, X, K, signs, xq, x_scale);
-  else
-    hipLaunchKernelGGL(k_act_rht_quant, grid, block, 0, stream, X, K, signs, xq, x_scale);
+  const int nchunk = K / 4;  // float4 chunks of a row
+  const dim3 grid(M);
+#define SVG_ACT(NT, CPT) \
+  hipLaunchKernelGGL((k_act_rht_quant<NT, CPT>), grid, dim3(NT), 0, stream, X, K, signs, xq, x_scale)
+  if (nchunk <= 256) SVG_ACT(256, 1);
+  else if (nchunk <= 512) SVG_ACT(512, 1);
+  else if (nchunk <= 1024) SVG_ACT(1024, 1);
+  else if (nchunk <= 2048) SVG_ACT(1024, 2);
+  else if (nchunk <= 4096) SVG_ACT(1024, 4);
+  else SVG_ACT(1024, 8);  // past 8192 chunks the row is read twice
+#undef SVG_ACT
   return hipGetLastError();
 }
 

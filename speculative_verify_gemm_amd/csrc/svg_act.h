@@ -1,0 +1,184 @@
+// Activation rotation and int8 quantization of one token row by one workgroup
+// (any multiple of 64 threads up to 1024).  Used by the stand-alone
+// act_rht_quant_i8 kernel and by the linear kernels that quantize their own
+// input rows.
+//
+// Source: "Karpathy's Trick for Faster Local LLMs Finally Has Proper Tooling"
+// (blog.dailydoseofds.com), section "How Uzu optimizes bytes and tokens per
+// pass": random sign flips, then a +/-1 Hadamard on each block of 32 values,
+// then 8-bit quantization on the fly.  Per token: amax = max |u|,
+// sigma = amax / 127, q = clamp(rint(u / sigma), -127, 127), stored scale
+// sigma * 2^-5 (the transform's overall scale on both operands).
+//
+// Thread i holds float4 chunks i, i + NT, i + 2 NT, ... (NT threads), so a
+// 32-block spans 8 consecutive lanes and the butterfly is lane exchanges only.
+//
+// The code of every value is the one IEEE division u / sigma (correctly
+// rounded) followed by round-half-to-even gives.  Dividing is slow, so the
+// quotient is first estimated as t = u * (1 / sigma): |t - u/sigma| <= 2^-16
+// for |u/sigma| <= 128, and the correctly rounded quotient is within 2^-18 of
+// u/sigma.  Unless t lies within 2^-13 of a half-integer, both round to the
+// same integer as t, so rint(t) is the code; near a half-integer (about one
+// value in 4000) the exact division decides.
+#pragma once
+#include "svg_device.h"
+
+#pragma clang fp contract(off)
+
+SVG_DEV int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// int8 code of u for the scale sigma (> 0); rinv = 1 / sigma; `fast` is false
+// when 1 / sigma is not a normal float (then every code divides).
+SVG_DEV int act_code(float u, float sigma, float rinv, bool fast) {
+  if (fast) {
+    const float t = u * rinv;
+    const float f = t - floorf(t);  // exact
+    if (fabsf(f - 0.5f) > 0x1p-13f) return clamp_i((int)rintf(t), -127, 127);
+  }
+  return clamp_i((int)rintf(u / sigma), -127, 127);
+}
+
+// Max over the workgroup (exact: max is order-free).  red: >= 16 floats of LDS.
+SVG_DEV float wg_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();  // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < nw; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// Rotated values of float4 chunk c of a row: loads (zeros past the row),
+// sign flip, 32-wide butterfly.
+SVG_DEV void act_rotate4(rsrc_t xr, rsrc_t sr, u32 c, float e[4]) {
+  const u32x4 v = bload16(xr, c * 16u);
+  const int sg = (int)bload4(sr, c * 4u);
+  e[0] = __uint_as_float(v[0]); e[1] = __uint_as_float(v[1]);
+  e[2] = __uint_as_float(v[2]); e[3] = __uint_as_float(v[3]);
+  apply_signs4(e[0], e[1], e[2], e[3], sg);
+  fwht32_lane4(e[0], e[1], e[2], e[3]);
+}
+
+SVG_DEV u32 pack4(const int q[4]) {
+  return (u32)(q[0] & 0xFF) | ((u32)(q[1] & 0xFF) << 8) | ((u32)(q[2] & 0xFF) << 16) |
+         ((u32)(q[3] & 0xFF) << 24);
+}
+
+// Where act_quant_row puts its results: packed code words and the row scale.
+// StoreGlobal<AUX>: global memory through buffer stores with cache policy AUX
+// (0, or kDeviceCoherent when other workgroups of the same launch read the
+// results: the stores then write through to the device's point of coherence
+// instead of staying in this XCD's L2).  StoreLds: a row of LDS words.
+constexpr int kDeviceCoherent = 16;  // sc1: device scope
+
+template <int AUX>
+struct StoreGlobal {
+  rsrc_t out, sc;
+  SVG_DEV StoreGlobal(int8_t* row, float* scale, int K)
+      : out(make_rsrc(row, (u32)K)), sc(make_rsrc(scale, 4u)) {}
+  SVG_DEV void word(u32 c, u32 v) const { __builtin_amdgcn_raw_buffer_store_b32(v, out, 4u * c, 0u, AUX); }
+  SVG_DEV void scale(float v) const { __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), sc, 0u, 0u, AUX); }
+};
+
+struct StoreLds {
+  u32* row;     // LDS, K/4 words
+  float* sc;    // LDS
+  SVG_DEV void word(u32 c, u32 v) const { row[c] = v; }
+  SVG_DEV void scale(float v) const { *sc = v; }
+};
+
+// A row's raw inputs held in registers: chunks threadIdx.x + NT * i, i < CPT
+// (chunks past the row are zeros), and their sign words.
+template <int CPT>
+struct RowRegs {
+  float e[CPT][4];
+  int sg[CPT];
+};
+
+// Request the loads of row x (K values) into r; nothing is waited for.
+template <int CPT>
+SVG_DEV void act_load_row(const float* x, int K, const int8_t* signs, RowRegs<CPT>& r) {
+  const u32 NT = blockDim.x;
+  const rsrc_t xr = make_rsrc(x, (u32)K * 4u);
+  const rsrc_t sr = make_rsrc(signs, (u32)K);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const u32 c = threadIdx.x + NT * i;
+    const u32x4 v = bload16(xr, c * 16u);
+    r.sg[i] = (int)bload4(sr, c * 4u);
+    r.e[i][0] = __uint_as_float(v[0]); r.e[i][1] = __uint_as_float(v[1]);
+    r.e[i][2] = __uint_as_float(v[2]); r.e[i][3] = __uint_as_float(v[3]);
+  }
+}
+
+// Rotate and quantize a row loaded by act_load_row (K <= 4 * NT * CPT); codes
+// and the scale go to `st`.  Every thread of the workgroup must call it.
+template <int CPT, class Store>
+SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* red) {
+  const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    apply_signs4(r.e[i][0], r.e[i][1], r.e[i][2], r.e[i][3], r.sg[i]);
+    fwht32_lane4(r.e[i][0], r.e[i][1], r.e[i][2], r.e[i][3]);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(r.e[i][0]), fabsf(r.e[i][1])), fmaxf(fabsf(r.e[i][2]), fabsf(r.e[i][3]))));
+  }
+  amax = wg_max(amax, red);
+  const float sigma = amax / 127.0f;
+  const float rinv = 1.0f / sigma;
+  const bool fast = sigma >= 0x1p-125f;
+  if (threadIdx.x == 0) st.scale(sigma * 0.03125f);  // exact: carries the transform's 2^-5
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const u32 c = threadIdx.x + NT * i;
+    if (c < nchunk) {
+      int q[4] = {0, 0, 0, 0};
+      if (amax > 0.f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) q[t] = act_code(r.e[i][t], sigma, rinv, fast);
+      }
+      st.word(c, pack4(q));
+    }
+  }
+}
+
+// Rotate and quantize row `x` (K values, K % 32 == 0); codes and the scale
+// go to `st`.  Every thread of the workgroup must call it.  The row is held
+// in registers when K <= 4 * NT * CPT (one read of the input); longer rows
+// are read twice (the second pass recomputes the same rotated values).
+template <int CPT, class Store>
+SVG_DEV void act_quant_row(const float* x, int K, const int8_t* signs, const Store& st, float* red) {
+  const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
+  if (nchunk <= NT * CPT) {
+    RowRegs<CPT> r;
+    act_load_row<CPT>(x, K, signs, r);
+    act_quant_loaded<CPT>(r, K, st, red);
+    return;
+  }
+  const rsrc_t xr = make_rsrc(x, (u32)K * 4u);
+  const rsrc_t sr = make_rsrc(signs, (u32)K);
+  float amax = 0.f;
+  for (u32 c = threadIdx.x; c < nchunk; c += NT) {
+    float e[4];
+    act_rotate4(xr, sr, c, e);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))));
+  }
+  amax = wg_max(amax, red);
+  const float sigma = amax / 127.0f;
+  const float rinv = 1.0f / sigma;
+  const bool fast = sigma >= 0x1p-125f;
+  if (threadIdx.x == 0) st.scale(sigma * 0.03125f);
+  for (u32 c = threadIdx.x; c < nchunk; c += NT) {
+    float e[4];
+    act_rotate4(xr, sr, c, e);
+    int q[4] = {0, 0, 0, 0};
+    if (amax > 0.f) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) q[t] = act_code(e[t], sigma, rinv, fast);
+    }
+    st.word(c, pack4(q));
+  }
+}

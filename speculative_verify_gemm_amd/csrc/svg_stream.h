@@ -33,6 +33,7 @@
 #pragma once
 #include <algorithm>
 
+#include "svg_act.h"
 #include "svg_device.h"
 #include "svg_internal.h"
 
@@ -52,13 +53,18 @@ struct LinArgs {
 
 // Step Q of a tile: issue the next batch's loads (the tile's batch Q+1, or the
 // first batch of the next tile), then consume batch Q.  `cur` holds batch Q.
-template <class P, int CPW, int U, int Q>
+// SKIP0: the loads of step 0 were issued earlier (see stream_tiles_resident).
+template <class P, int CPW, int U, int Q, bool SKIP0 = false>
 struct TileSteps {
+  template <class B>
+  static SVG_DEV void issue_next(P& p, B& nxt, int t, int tn, int ntiles, int sb) {
+    constexpr bool last = Q + 1 == CPW / U;
+    p.template load<U>(nxt, last ? tn : t, last ? sb : sb + (Q + 1) * U, !last || tn < ntiles);
+  }
   template <class B, class X>
   static SVG_DEV void run(P& p, B& cur, B& nxt, const X& acts, int t, int tn, int ntiles, int sb) {
-    constexpr int NB = CPW / U;
-    constexpr bool last = Q + 1 == NB;
-    p.template load<U>(nxt, last ? tn : t, last ? sb : sb + (Q + 1) * U, !last || tn < ntiles);
+    constexpr bool last = Q + 1 == CPW / U;
+    if constexpr (!(SKIP0 && Q == 0)) issue_next(p, nxt, t, tn, ntiles, sb);
     __builtin_amdgcn_sched_barrier(0);
     p.template compute<U, Q * U>(cur, acts, t, sb + Q * U);
     __builtin_amdgcn_sched_barrier(0);
@@ -66,44 +72,61 @@ struct TileSteps {
   }
 };
 
-template <class P, int CPW, int U>
-SVG_DEV void stream_tiles_resident(P& p, int ntiles) {
+// The workgroup walks tiles first, first + stride, ...  `pre()` runs before
+// the first weight batch is requested and `gate()` after it, before the
+// activations are read (the fused kernel quantizes its input rows there).  With LDS, the
+// activation operands come from the workgroup's own LDS copy of the quantized
+// rows (P::load_acts<NC, true>) instead of global memory, and the second batch
+// is requested before the gate too, so that two batches stream while the
+// rows are being quantized.  (With global activations the second batch waits:
+// loads complete in order, so activations requested after it would hold the
+// first computation back.)
+template <class P, int CPW, int U, bool LDS, class Pre, class Gate>
+SVG_DEV void stream_tiles_resident(P& p, int ntiles, int first, int stride, Pre&& pre, Gate&& gate) {
   static_assert(CPW % U == 0, "batches must tile a wave's chunks");
   constexpr int NB = CPW / U;
   using B = typename P::template Batch<U>;
   using Steps = TileSteps<P, CPW, U, 0>;
-  int t = blockIdx.x;
+  int t = first;
   if (t >= ntiles) return;  // uniform over the workgroup
   const int sb = p.wave * CPW;
-  typename P::template Acts<CPW> acts;
-  p.template load_acts<CPW>(acts, sb);
+  int tn = t + stride;
   B b0, b1;
+  pre();
+  __builtin_amdgcn_sched_barrier(0);
   p.template load<U>(b0, t, sb, true);
+  if constexpr (LDS) Steps::issue_next(p, b1, t, tn, ntiles, sb);
+  __builtin_amdgcn_sched_barrier(0);
+  gate();
+  typename P::template Acts<CPW> acts;
+  p.template load_acts<CPW, LDS>(acts, sb);
+  TileSteps<P, CPW, U, 0, LDS>::run(p, b0, b1, acts, t, tn, ntiles, sb);
+  p.finish(t, 0);
   // Two tiles per iteration: with an odd number of batches per tile the next
   // tile's first batch lands in the other buffer.
   for (;;) {
-    int tn = t + (int)gridDim.x;
-    Steps::run(p, b0, b1, acts, t, tn, ntiles, sb);
-    p.finish(t, 0);
     if (tn >= ntiles) break;
     t = tn;
-    tn = t + (int)gridDim.x;
+    tn = t + stride;
     if constexpr (NB % 2 == 0) Steps::run(p, b0, b1, acts, t, tn, ntiles, sb);
     else Steps::run(p, b1, b0, acts, t, tn, ntiles, sb);
     p.finish(t, 1);
     if (tn >= ntiles) break;
     t = tn;
+    tn = t + stride;
+    Steps::run(p, b0, b1, acts, t, tn, ntiles, sb);
+    p.finish(t, 0);
   }
 }
 
-template <class P>
-SVG_DEV void stream_tiles_simple(P& p, int ntiles, int sb, int se) {
+template <class P, bool LDS>
+SVG_DEV void stream_tiles_simple(P& p, int ntiles, int first, int stride, int sb, int se) {
   int slot = 0;
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  for (int t = first; t < ntiles; t += stride) {
     for (int j = sb; j < se; ++j) {
       typename P::template Acts<1> acts;
       typename P::template Batch<1> b;
-      p.template load_acts<1>(acts, j);
+      p.template load_acts<1, LDS>(acts, j);
       p.template load<1>(b, t, j, true);
       p.template compute<1, 0>(b, acts, t, j);
     }
@@ -112,20 +135,78 @@ SVG_DEV void stream_tiles_simple(P& p, int ntiles, int sb, int se) {
   }
 }
 
-template <class P, int WAVES, int CPW, int U>
-__global__ __launch_bounds__(WAVES * 64) void k_linear(LinArgs a) {
-  __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
+template <class P, int WAVES, int CPW, int U, bool LDS = false, class Pre, class Gate>
+SVG_DEV void stream_tiles(P& p, const LinArgs& a, int first, int stride, Pre&& pre, Gate&& gate) {
   const int ntiles = (a.N + kTileRows - 1) / kTileRows;
-  P p;
-  p.template init<WAVES>(a, red);
   if constexpr (CPW > 0) {
-    stream_tiles_resident<P, CPW, U>(p, ntiles);
+    stream_tiles_resident<P, CPW, U, LDS>(p, ntiles, first, stride, pre, gate);
   } else {
+    if (first >= ntiles) return;
+    pre();
+    gate();
     const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
     const int per = (KT + WAVES - 1) / WAVES;
     const int sb = min(KT, p.wave * per);
-    stream_tiles_simple<P>(p, ntiles, sb, min(KT, sb + per));
+    stream_tiles_simple<P, LDS>(p, ntiles, first, stride, sb, min(KT, sb + per));
   }
+}
+
+template <class P, int WAVES, int CPW, int U>
+__global__ __launch_bounds__(WAVES * 64) void k_linear(LinArgs a) {
+  __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
+  P p;
+  p.template init<WAVES>(a, red);
+  stream_tiles<P, WAVES, CPW, U>(p, a, blockIdx.x, gridDim.x, [] {}, [] {});
+}
+
+// ------------------------------------------------------ fused activation input
+// The fused kernel takes the fp32 activation rows X of a GEMV-sized call
+// (one or two rows), and every workgroup rotates and quantizes them itself
+// into LDS while its first weight batch is in flight, then reads its
+// activation operands from there: no launch of its own for the quantization
+// and nothing shared between workgroups.  Workgroup 0 also writes xq and
+// x_scale (the values act_rht_quant_i8 gives).  K <= kLdsMaxK.
+//
+// Larger M is not fused this way: each workgroup would quantize all M rows
+// (M x K values) for itself.  Publishing the rows from a few workgroups to
+// the others inside one launch was measured slower than a separate launch:
+// the publishers' loads of X queue behind the other workgroups' weight
+// stream, and the readers' polls too.
+constexpr int kLdsMaxK = 12288;
+
+struct ActIn {
+  const float* X;
+  const int8_t* signs;
+};
+
+template <class P, int WAVES, int CPW, int U>
+__global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f) {
+  static_assert(P::kMaxTok <= 2, "fused quantization is for one or two rows");
+  __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
+  __shared__ float act_red[16];
+  __shared__ __align__(16) u32 xl[P::kMaxTok * kLdsMaxK / 4];
+  __shared__ float xsl[P::kMaxTok];
+  P p;
+  p.template init<WAVES>(a, red);
+  const int KP = ((a.K + 127) >> 7) * 32;  // words per LDS row: K padded to whole 128-k chunks
+  stream_tiles<P, WAVES, CPW, U, true>(p, a, blockIdx.x, gridDim.x, [] {}, [&] {
+    // zero the padding (rows past M, k past K), quantize the rows.  (Reading
+    // the rows before the weights were requested was measured slower: every
+    // workgroup's row loads then delay the start of the weight stream.)
+    for (int i = threadIdx.x; i < P::kMaxTok * KP; i += blockDim.x)
+      if (i / KP >= a.M || (i % KP) * 4 >= a.K) xl[i] = 0u;
+    for (int m = 0; m < a.M; ++m)
+      act_quant_row<4>(f.X + (size_t)m * a.K, a.K, f.signs, StoreLds{xl + m * KP, xsl + m}, act_red);
+    __syncthreads();
+    if (blockIdx.x == 0) {  // the call's xq / x_scale outputs
+      for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x)
+        reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[i] = xl[(i / (a.K / 4)) * KP + i % (a.K / 4)];
+      if (threadIdx.x < a.M) const_cast<float*>(a.x_scale)[threadIdx.x] = xsl[threadIdx.x];
+    }
+    p.xlds = reinterpret_cast<const int8_t*>(xl);
+    p.xlds_row = KP * 4;
+    p.x_scale = xsl;
+  });
 }
 
 // Workgroups resident on the device at once for a kernel (cached per kernel:
@@ -144,14 +225,29 @@ int resident_blocks(int block) {
 // Persistent grid: at most as many workgroups as fit at once, and the tiles
 // spread evenly (every workgroup walks the same number of tiles, give or take
 // one) so none is left with a tail of its own.
-template <class P, int WAVES, int CPW, int U>
-hipError_t launch_linear(const LinArgs& a, hipStream_t stream) {
-  constexpr auto kernel = k_linear<P, WAVES, CPW, U>;
-  const int ntiles = (a.N + kTileRows - 1) / kTileRows;
-  const int cap = resident_blocks<kernel>(WAVES * 64);
+template <auto KERNEL>
+int spread_grid(int ntiles, int block) {
+  const int cap = resident_blocks<KERNEL>(block);
   const int rounds = (ntiles + cap - 1) / cap;
-  const int grid = std::max(1, (ntiles + rounds - 1) / rounds);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(WAVES * 64), 0, stream, a);
+  return std::max(1, (ntiles + rounds - 1) / rounds);
+}
+
+// f != nullptr (GEMV policies only): the fused kernel.
+template <class P, int WAVES, int CPW, int U>
+hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
+  const int ntiles = (a.N + kTileRows - 1) / kTileRows;
+  if constexpr (P::kMaxTok <= 2) {
+    if (f) {
+      constexpr auto kernel = k_linear_fused<P, WAVES, CPW, U>;
+      hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream,
+                         a, *f);
+      return hipGetLastError();
+    }
+  }
+  {
+    constexpr auto kernel = k_linear<P, WAVES, CPW, U>;
+    hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -165,11 +261,17 @@ hipError_t launch_linear(const LinArgs& a, hipStream_t stream) {
 // its CU.  K ranges that
 // fit no shape take the plain loop.
 template <class P>
-hipError_t launch_linear_auto(const LinArgs& a, hipStream_t stream) {
+hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
+  if (f && (P::kMaxTok > 2 || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
+    hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, const_cast<int8_t*>(a.xq),
+                                            const_cast<float*>(a.x_scale), stream);
+    if (e != hipSuccess) return e;
+    f = nullptr;
+  }
 #define SVG_FITS(CPW, U, LIM) (P::kActRegs * (CPW) + 2 * (U) * P::kBatchRegs + P::kFixedRegs <= (LIM))
 #define SVG_TRY(W, CPW, U, LIM) \
-  if constexpr (SVG_FITS(CPW, U, LIM)) return launch_linear<P, W, CPW, U>(a, stream)
+  if constexpr (SVG_FITS(CPW, U, LIM)) return launch_linear<P, W, CPW, U>(a, f, stream)
   if (KT <= 8) { SVG_TRY(8, 1, 1, 192); }
   if (KT <= 16) { SVG_TRY(8, 2, 2, 128); else SVG_TRY(8, 2, 1, 192); }
   if (KT <= 32) { SVG_TRY(8, 4, 4, 128); else SVG_TRY(8, 4, 2, 192); }
@@ -179,5 +281,5 @@ hipError_t launch_linear_auto(const LinArgs& a, hipStream_t stream) {
   if (KT <= 192) { SVG_TRY(16, 12, 4, 128); else SVG_TRY(16, 12, 2, 128); }
 #undef SVG_TRY
 #undef SVG_FITS
-  return launch_linear<P, 8, 0, 1>(a, stream);
+  return launch_linear<P, 8, 0, 1>(a, f, stream);
 }

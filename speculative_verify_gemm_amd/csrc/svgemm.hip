@@ -125,10 +125,13 @@ svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs, i
                                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
-svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
-                       const uint16_t* w_scale, const void* w_zero, int fmt, int group, int N,
-                       float* y, int32_t* partials_debug, void* stream) {
-  static const char* fn = "w4a8_linear";
+}  // extern "C"
+
+namespace {
+
+svg_status check_w4(const char* fn, const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
+                    const uint16_t* w_scale, const void* w_zero, int fmt, int group, int N, float* y,
+                    int32_t* partials_debug) {
   if (M < 0 || N < 0) return fail(SVG_EINVAL, fn, "M < 0 or N < 0");
   if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
   if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16) return fail(SVG_EUNSUPPORTED, fn, "fmt must be a W4 format");
@@ -140,16 +143,11 @@ svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (!aligned(x_scale, 4) || !aligned(y, 4) || !aligned(w_scale, 4) ||
       (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 4)) || (partials_debug && !aligned(partials_debug, 4)))
     return fail(SVG_EALIGN, fn, "misaligned scale, zero, y or partials pointer");
-  if (M == 0 || N == 0) return ok();
-  return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
-                                        group, N, y, partials_debug,
-                                        reinterpret_cast<hipStream_t>(stream)));
+  return SVG_OK;
 }
 
-svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
-                       const uint16_t* w_scale, int N, float* y, int32_t* partials_debug,
-                       void* stream) {
-  static const char* fn = "w8a8_linear";
+svg_status check_w8(const char* fn, const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
+                    const uint16_t* w_scale, int N, float* y, int32_t* partials_debug) {
   if (M < 0 || N < 0) return fail(SVG_EINVAL, fn, "M < 0 or N < 0");
   if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
   if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
@@ -160,9 +158,71 @@ svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (!aligned(x_scale, 4) || !aligned(y, 4) || !aligned(w_scale, 2) ||
       (partials_debug && !aligned(partials_debug, 4)))
     return fail(SVG_EALIGN, fn, "misaligned scale, y or partials pointer");
+  return SVG_OK;
+}
+
+// The fp32 input of the fused calls: X, signs and block.
+svg_status check_fused_input(const char* fn, const float* X, const int8_t* signs, int block) {
+  if (!X || !signs) return fail(SVG_EINVAL, fn, "null required pointer");
+  if (block != 32) return fail(SVG_EUNSUPPORTED, fn, "block must be 32");
+  if (!aligned(X, 16)) return fail(SVG_EALIGN, fn, "X needs 16-byte alignment");
+  if (!aligned(signs, 4)) return fail(SVG_EALIGN, fn, "signs needs 4-byte alignment");
+  return SVG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
+                       const uint16_t* w_scale, const void* w_zero, int fmt, int group, int N,
+                       float* y, int32_t* partials_debug, void* stream) {
+  static const char* fn = "w4a8_linear";
+  svg_status st = check_w4(fn, xq, x_scale, M, K, wq, w_scale, w_zero, fmt, group, N, y, partials_debug);
+  if (st != SVG_OK) return st;
   if (M == 0 || N == 0) return ok();
-  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug,
+  return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
+                                        group, N, y, partials_debug, nullptr, nullptr,
                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
+                       const uint16_t* w_scale, int N, float* y, int32_t* partials_debug,
+                       void* stream) {
+  static const char* fn = "w8a8_linear";
+  svg_status st = check_w8(fn, xq, x_scale, M, K, wq, w_scale, N, y, partials_debug);
+  if (st != SVG_OK) return st;
+  if (M == 0 || N == 0) return ok();
+  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, nullptr,
+                                        nullptr, reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
+                                 int8_t* xq, float* x_scale, const uint8_t* wq, const uint16_t* w_scale,
+                                 const void* w_zero, int fmt, int group, int N, float* y,
+                                 int32_t* partials_debug, void* stream) {
+  static const char* fn = "act_quant_w4a8_linear";
+  svg_status st = check_w4(fn, xq, x_scale, M, K, wq, w_scale, w_zero, fmt, group, N, y, partials_debug);
+  if (st == SVG_OK) st = check_fused_input(fn, X, signs, block);
+  if (st != SVG_OK) return st;
+  if (M == 0) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, xq, x_scale, s));
+  return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
+                                        group, N, y, partials_debug, X, signs, s));
+}
+
+svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
+                                 int8_t* xq, float* x_scale, const int8_t* wq, const uint16_t* w_scale,
+                                 int N, float* y, int32_t* partials_debug, void* stream) {
+  static const char* fn = "act_quant_w8a8_linear";
+  svg_status st = check_w8(fn, xq, x_scale, M, K, wq, w_scale, N, y, partials_debug);
+  if (st == SVG_OK) st = check_fused_input(fn, X, signs, block);
+  if (st != SVG_OK) return st;
+  if (M == 0) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, xq, x_scale, s));
+  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, X, signs, s));
 }
 
 }  // extern "C"

@@ -60,19 +60,23 @@ def _short(name):
 
 
 def _is_linear(name):
-    return name.startswith("k_linear<")
+    return name.startswith(("k_linear<", "k_linear_fused<"))
 
 
 def _policy(name):
-    """'k_linear<MfmaW4<1, 64, false, false>, 8, 4, 4>' -> 'MfmaW4<1, 64, false, false>'."""
-    inner = name[len("k_linear<"):]
+    """'k_linear<MfmaW4<1, 64, false, false>, 8, 4, 4>' -> 'k_linear<MfmaW4<1, 64, false, false>>'."""
+    head, inner = name.split("<", 1)
+    return f"{head}<{_first_arg(inner)}>"
+
+
+def _first_arg(inner):
     depth = 0
     for i, c in enumerate(inner):
         depth += c == "<"
         depth -= c == ">"
         if c == "," and depth == 0:
             return inner[:i]
-    return inner
+    return inner.rstrip(">")
 
 
 def trace_summary(d, cmd):

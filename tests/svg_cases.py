@@ -84,3 +84,44 @@ def host(t):
 
 def f16_bits(a):
     return np.asarray(a).view(np.uint16) if np.asarray(a).dtype == np.float16 else np.asarray(a)
+
+
+def gpu_fused(x, signs, w, debug=True):
+    """act_quant_w4a8_linear / act_quant_w8a8_linear on host inputs x [M,K]:
+    returns (xq, x_scale, y, partials)."""
+    xd = x if isinstance(x, torch.Tensor) else to_dev(x)
+    sd = signs if isinstance(signs, torch.Tensor) else to_dev(signs)
+    M, K = xd.shape
+    N = w["N"]
+    xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    xs = torch.empty((M,), dtype=torch.float32, device=DEV)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    if w["fmt"] == "w8":
+        dbg = torch.empty((M, N), dtype=torch.int32, device=DEV) if debug else None
+        svg.act_quant_w8a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], N, y, dbg)
+    else:
+        dbg = torch.empty((M, N, K // w["group"]), dtype=torch.int32, device=DEV) if debug else None
+        svg.act_quant_w4a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], w["wz"], w["fmt"], w["group"], N, y, dbg)
+    return xq, xs, y, dbg
+
+
+def tie_rows(M, K, seed, exp=-3, nudge=False):
+    """Activation rows whose rotated values are exact half-integer multiples of
+    the row scale 2^exp (ties of the int8 rounding), one value 127 * 2^exp per
+    row so that the scale is exactly 2^exp; with nudge, each target moved by
+    one fp32 ulp up or down (near-ties).  Built as x = D H u / 32 blockwise
+    in fp64 with the oracle's butterfly (H H = 32 I), then cast to fp32.
+    Input construction only: the expected codes come from the oracle."""
+    from oracle import svg_oracle as O
+    rng = np.random.default_rng(seed)
+    u = (rng.integers(-127, 127, size=(M, K)) + 0.5) * 2.0 ** exp
+    u[:, 0] = 127 * 2.0 ** exp
+    if nudge:
+        up = rng.integers(0, 2, size=(M, K)).astype(bool)
+        u32 = u.astype(np.float32)
+        u = np.where(up, np.nextafter(u32, np.float32(np.inf)), np.nextafter(u32, np.float32(-np.inf)))
+        u = u.astype(np.float64)
+        u[:, 0] = 127 * 2.0 ** exp
+    signs = np.where(rng.integers(0, 2, size=K) == 0, 1, -1).astype(np.int8)
+    x = O.fwht32(u) * signs.astype(np.float64) / 32.0
+    return x.astype(np.float32), signs

@@ -29,8 +29,8 @@ def svg():
 
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
-        ["act_rht_quant_i8", "rht_rotate_weights", "svg_last_error", "svg_weight_sizes",
-         "w4a8_linear", "w8a8_linear"])
+        ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
+         "svg_last_error", "svg_weight_sizes", "w4a8_linear", "w8a8_linear"])
 
 
 def test_library_exports_every_declared_symbol(svg):
@@ -105,6 +105,41 @@ def test_rotate_validation(svg, args, code):
 ])
 def test_w8a8_validation(svg, args, code):
     assert svg.lib.w8a8_linear(*args, NULL) == code
+
+
+def _fused4(svg, **kw):
+    args = dict(X=A, M=1, K=128, signs=A, block=32, xq=A, xs=A, wq=A, ws=A, wz=A, fmt=1, g=64, N=16, y=A,
+                dbg=NULL)
+    args.update(kw)
+    return svg.lib.act_quant_w4a8_linear(args["X"], args["M"], args["K"], args["signs"], args["block"],
+                                         args["xq"], args["xs"], args["wq"], args["ws"], args["wz"],
+                                         args["fmt"], args["g"], args["N"], args["y"], args["dbg"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=NULL), 1), (dict(signs=NULL), 1), (dict(xq=NULL), 1), (dict(wz=NULL), 1),
+    (dict(block=64), 2), (dict(M=33), 2), (dict(g=96), 2), (dict(fmt=2), 2),
+    (dict(X=MIS), 3), (dict(xq=MIS), 3), (dict(signs=MIS), 3), (dict(wq=MIS), 3),
+])
+def test_fused_w4_validation(svg, kw, code):
+    assert _fused4(svg, **kw) == code
+    assert svg.last_error().startswith("act_quant_w4a8_linear:")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NULL, 1, 64, A, 32, A, A, A, A, 8, A, NULL), 1),         # X
+    ((A, 1, 64, A, 16, A, A, A, A, 8, A, NULL), 2),            # block
+    ((A, 1, 131104, A, 32, A, A, A, A, 8, A, NULL), 2),        # K too large for int32 sums
+    ((A, 1, 64, MIS, 32, A, A, A, A, 8, A, NULL), 3),          # signs alignment
+])
+def test_fused_w8_validation(svg, args, code):
+    assert svg.lib.act_quant_w8a8_linear(*args, NULL) == code
+    assert svg.last_error().startswith("act_quant_w8a8_linear:")
+
+
+def test_fused_empty_calls_are_ok(svg):
+    assert _fused4(svg, M=0) == 0 and svg.last_error() == ""
+    assert svg.lib.act_quant_w8a8_linear(A, 0, 64, A, 32, A, A, A, A, 8, A, NULL, NULL) == 0
 
 
 def test_weight_sizes_match_the_oracle_layout(svg):

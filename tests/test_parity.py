@@ -26,8 +26,9 @@ TOL = 2e-3
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    global C
+    global C, svg
     import svg_cases as C  # noqa: F401  (imports the binding, which loads libsvgemm)
+    import speculative_verify_gemm_amd as svg
 
 
 def check_y(y, y_ref, tol=TOL):
@@ -177,3 +178,124 @@ def test_rejects_bad_arguments_without_writing():
         svg.w4a8_linear(xq, xs, wq, ws, wz, "w4_z16", 48, 8, y)
     assert ei.value.status == svg.SVG_EUNSUPPORTED
     assert torch.all(y == 7.0)
+
+
+# ------------------------------------------------------------- rounding ties
+@pytest.mark.parametrize("nudge", [False, True])
+def test_act_codes_at_rounding_ties(nudge):
+    """Rotated values exactly on (or one ulp off) half-integer multiples of the
+    row scale: the int8 rounding must follow the IEEE quotient and
+    round-half-to-even bit for bit, in the stand-alone and the fused kernels."""
+    M, K, N = 4, 2048, 48
+    C.say(f"act codes at ties nudge={nudge}")
+    x, signs = C.tie_rows(M, K, seed=5 + int(nudge), nudge=nudge)
+    qx, sx = O.quant_acts(x, signs)
+    xq, xs = C.gpu_quant_acts(x, signs)
+    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+    _x, W, _s = synth.random_case(1, N, K, seed=77)
+    w = C.oracle_weights_to_dev(O.prepare_w4(W, signs, 64), "w4_z16")
+    fq, fs, _y, _d = C.gpu_fused(x, signs, w)
+    assert np.array_equal(C.host(fq), qx)
+    assert np.array_equal(C.host(fs).view(np.uint32), sx.view(np.uint32))
+
+
+# ------------------------------------------------------------- fused calls
+FUSED_CASES = [("w4_z16", 64, M, 37, 384) for M in (1, 2, 3, 16, 17, 32)]
+FUSED_CASES += [("w4_z4", 32, 1, 50, 96), ("w4_z4", 32, 5, 50, 96), ("w4_z16", 128, 32, 130, 12288),
+                ("w4_z16", 64, 16, 300, 4096), ("w4_z16", 64, 1, 64, 12288), ("w4_z16", 64, 32, 40, 320),
+                ("w4_z4", 128, 2, 20, 384)]
+FUSED_CASES += [("w8", 0, M, 37, 384) for M in (1, 2, 16, 32)]
+FUSED_CASES += [("w8", 0, 32, 70, 12288), ("w8", 0, 1, 33, 12288)]
+
+
+@pytest.mark.parametrize("fmt,group,M,N,K", FUSED_CASES)
+def test_fused_matches_oracle(fmt, group, M, N, K):
+    """act_quant_w4a8_linear / act_quant_w8a8_linear (one launch for M <= 2,
+    two otherwise): activation codes and scales bit-exact, partial sums
+    bit-exact, y within tolerance."""
+    C.say(f"fused fmt={fmt} g={group} M={M} N={N} K={K}")
+    x, W, signs = synth.random_case(M, N, K, seed=11 * M + N + K + group, x_kind="student_t3")
+    if fmt == "w8":
+        ow = O.prepare_w8(W, signs)
+        y_ref, S_ref, qx, sx = O.linear_w8(x, signs, ow)
+    else:
+        ow = O.prepare_w4(W, signs, group)
+        y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
+    w = C.oracle_weights_to_dev(ow, fmt)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+    assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
+    check_y(C.host(y), y_ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 16])
+def test_fused_repeats_on_new_inputs(M):
+    """Consecutive fused calls, each on new activations written to the same xq
+    buffer: every call matches the two-launch path bit for bit."""
+    C.say(f"fused repeats M={M}")
+    N, K = 96, 1024
+    _x, W, signs = synth.random_case(M, N, K, seed=123)
+    xs_in = [synth.random_case(M, N, K, seed=500 + i, x_kind="student_t3")[0] for i in range(4)]
+    w4 = C.gpu_prepare(W, signs, "w4_z16", 64)
+    w8 = C.gpu_prepare(W, signs, "w8", 0)
+    sd = C.to_dev(signs)
+    xq = torch.empty((M, K), dtype=torch.int8, device=C.DEV)
+    xsc = torch.empty((M,), dtype=torch.float32, device=C.DEV)
+    ys = []
+    for i, x in enumerate(xs_in):
+        y = torch.empty((M, N), dtype=torch.float32, device=C.DEV)
+        if i % 2 == 0:
+            svg.act_quant_w4a8_linear(C.to_dev(x), sd, xq, xsc, w4["wq"], w4["ws"], w4["wz"], "w4_z16", 64, N, y)
+        else:
+            svg.act_quant_w8a8_linear(C.to_dev(x), sd, xq, xsc, w8["wq"], w8["ws"], N, y)
+        ys.append(y)
+    for i, x in enumerate(xs_in):
+        q, sc = C.gpu_quant_acts(x, signs)
+        ref, _ = C.gpu_linear(q, sc, w4 if i % 2 == 0 else w8, debug=False)
+        assert np.array_equal(C.host(ys[i]).view(np.uint32), C.host(ref).view(np.uint32)), i
+
+
+def test_fused_in_captured_graph():
+    """Two fused calls (M = 16: two launches; M = 1: one) captured in a HIP
+    graph and replayed several times, with eager fused calls in between:
+    every replay matches the eager results bit for bit."""
+    C.say("fused calls in a captured graph")
+    M, K = 16, 1024
+    x1, W1, s1 = synth.random_case(M, 80, K, seed=301)
+    x2, W2, s2 = synth.random_case(1, 48, K, seed=302)
+    wa = C.gpu_prepare(W1, s1, "w4_z16", 64)
+    wb = C.gpu_prepare(W2, s2, "w8", 0)
+    X1, S1, X2, S2 = C.to_dev(x1), C.to_dev(s1), C.to_dev(x2), C.to_dev(s2)
+    ref1 = C.host(C.gpu_fused(X1, S1, wa, debug=False)[2])
+    ref2 = C.host(C.gpu_fused(X2, S2, wb, debug=False)[2])
+    xq1 = torch.empty((M, K), dtype=torch.int8, device=C.DEV)
+    xs1 = torch.empty((M,), dtype=torch.float32, device=C.DEV)
+    y1 = torch.empty((M, 80), dtype=torch.float32, device=C.DEV)
+    xq2 = torch.empty((1, K), dtype=torch.int8, device=C.DEV)
+    xs2 = torch.empty((1,), dtype=torch.float32, device=C.DEV)
+    y2 = torch.empty((1, 48), dtype=torch.float32, device=C.DEV)
+
+    def run():
+        svg.act_quant_w4a8_linear(X1, S1, xq1, xs1, wa["wq"], wa["ws"], wa["wz"], "w4_z16", 64, 80, y1)
+        svg.act_quant_w8a8_linear(X2, S2, xq2, xs2, wb["wq"], wb["ws"], 48, y2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y1.fill_(-1.0)
+        y2.fill_(-1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.host(y1).view(np.uint32), ref1.view(np.uint32)), rep
+        assert np.array_equal(C.host(y2).view(np.uint32), ref2.view(np.uint32)), rep
+        C.gpu_fused(X1, S1, wa, debug=False)  # eager work in between
