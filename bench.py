@@ -7,7 +7,7 @@ and each of its four input spaces, the fp32 activation rows are rotated and
 quantized, and the linear(s) consuming them run (q/k/v stacked along N into
 one launch, gate/up into one).  By default each such step goes through
 act_quant_w4a8_linear / act_quant_w8a8_linear, which is ONE launch for
-M <= 2 (every workgroup quantizes the rows itself) and two otherwise;
+M = 1 (every workgroup quantizes the row itself) and two otherwise;
 --unfused always runs act_rht_quant_i8 and the linear as two launches.  Weights are rotated and
 quantized once at setup (rht_rotate_weights) and stay resident in HBM.  The
 pass is captured in a HIP graph and replayed.
@@ -206,13 +206,13 @@ def time_linear_launches(stack, io, g, ms_graph, steps):
     launch counts from the end of the previous one to its own end -- the span
     a kernel trace reports.  The kernel timed is the one that does the
     contraction: the fused kernel (which also quantizes its input) where the
-    pass fuses (M <= 2), else the linear alone on activations quantized once
-    before, untimed.  Before each step the captured pass is replayed enough
+    pass fuses (one launch per linear), else the linear alone on activations
+    quantized once before, untimed.  Before each step the captured pass is replayed enough
     times to keep the device busy while the host enqueues, so no host launch
     latency enters the timed spans.
     Returns (mean ms, mean algorithmic bytes, launches, {kind: mean us})."""
     torch = stack.torch
-    fused = stack.fused and io["M"] <= 2
+    fused = stack.fused and one_launch(io["M"], stack.group)
     t0 = time.perf_counter()
     stack.run_pass(io)                       # host cost of enqueuing one eager pass
     enqueue_ms = (time.perf_counter() - t0) * 1e3
@@ -242,19 +242,24 @@ def time_linear_launches(stack, io, g, ms_graph, steps):
             {n: round(v * 1e3, 3) for n, v in mean_kind.items()})
 
 
+def one_launch(M, group):
+    """Whether act_quant_*_linear quantizes inside the linear's launch."""
+    return M == 1 or (M <= 2 and group == 32)
+
+
 def kernel_name(fmt, group, M, fused):
     """The linear kernel template instance a launch of this format and M runs
     (k_linear[_fused]<policy, waves, chunks per wave, batch>; the shape varies
     with K)."""
     if fmt == "w8":
-        pol = f"DotW8<{M}>" if M <= 2 else f"MfmaW8<{1 if M <= 16 else 2}>"
+        pol = "DotW8<1>" if M <= 1 else f"MfmaW8<{1 if M <= 16 else 2}>"
     else:
         z4 = "true" if fmt == "w4_z4" else "false"
-        if M <= 2 or group == 32:
+        if M <= 1 or group == 32:
             pol = f"DotW4<{1 if M <= 1 else 2 if M <= 2 else 8}, {group}, {z4}, false>"
         else:
             pol = f"MfmaW4<{1 if M <= 16 else 2}, {group}, {z4}, false>"
-    return f"k_linear{'_fused' if fused and M <= 2 else ''}<{pol}, ...>"
+    return f"k_linear{'_fused' if fused and one_launch(M, group) else ''}<{pol}, ...>"
 
 
 def profiled_traffic(workload, M):
@@ -374,6 +379,7 @@ def main():
     print(f"[bench] linear launches: mean {kmean_ms * 1e3:.2f} us, {k_gbps:.1f} GB/s; per kind us {kmed}",
           file=sys.stderr, flush=True)
     traffic, traffic_src = profiled_traffic(args.workload, M)
+    one = stack.fused and one_launch(M, stack.group)
     ops_per_pass = sum(2 * M * N * K for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
     kops = ops_per_pass / (args.layers * len(LAYER_LAUNCHES))  # mean int ops per linear launch
     wbytes = sum(weight_bytes(N, K, stack.fmt, stack.group) for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
@@ -396,8 +402,8 @@ def main():
         "config": {"workload": args.workload, "description": spec["desc"], "M": M,
                    "layers": args.layers, "weight_format": stack.fmt, "group": stack.group,
                    "bytes_per_pass": nbytes, "weight_bytes_per_pass": wbytes,
-                   "launches_per_pass": args.layers * len(LAYER_LAUNCHES) * (1 if stack.fused and M <= 2 else 2),
-                   "fused_activation_quantization": stack.fused and M <= 2},
+                   "launches_per_pass": args.layers * len(LAYER_LAUNCHES) * (1 if one else 2),
+                   "fused_activation_quantization": one},
         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "passes_per_s": round(1e3 / ms, 2),
         "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1)},

@@ -193,7 +193,7 @@ def _check_fused(X, signs, xq, x_scale):
 
 def act_quant_w4a8_linear(X, signs, xq, x_scale, wq, w_scale, w_zero, fmt, group, N, y,
                           partials_debug=None, block=BLOCK, stream=None):
-    """act_rht_quant_i8 then w4a8_linear (one launch for M <= 2): fp32 X[M, K]
+    """act_rht_quant_i8 then w4a8_linear (one launch for M = 1): fp32 X[M, K]
     in, xq / x_scale (written) and y[M, N] out."""
     _check_fused(X, signs, xq, x_scale)
     f = _fmt(fmt)
@@ -215,7 +215,7 @@ def act_quant_w4a8_linear(X, signs, xq, x_scale, wq, w_scale, w_zero, fmt, group
 
 def act_quant_w8a8_linear(X, signs, xq, x_scale, wq, w_scale, N, y, partials_debug=None,
                           block=BLOCK, stream=None):
-    """act_rht_quant_i8 then w8a8_linear (one launch for M <= 2)."""
+    """act_rht_quant_i8 then w8a8_linear (one launch for M = 1)."""
     _check_fused(X, signs, xq, x_scale)
     _dev(xq, "xq", torch.int8)
     _dev(x_scale, "x_scale", torch.float32)

@@ -412,8 +412,8 @@ struct DotW4 : W4Common {
 template <int G, bool Z4, bool DBG>
 hipError_t dispatch_g(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   if (a.M <= 1) return launch_linear_auto<DotW4<1, G, Z4, DBG>>(a, f, stream);
-  if (a.M <= kGemvMaxM) return launch_linear_auto<DotW4<2, G, Z4, DBG>>(a, f, stream);
   if constexpr (G == 32) {
+    if (a.M <= 2) return launch_linear_auto<DotW4<2, G, Z4, DBG>>(a, f, stream);
     // no MFMA form for 32-wide groups: the dot kernel, 8 tokens per launch,
     // after a separate quantization of all rows when the input is fp32
     if (f) {

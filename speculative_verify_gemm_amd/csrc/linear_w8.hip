@@ -219,7 +219,6 @@ hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K,
   const ActIn fa{X, signs};
   const ActIn* f = X ? &fa : nullptr;
   if (M <= 1) return launch_linear_auto<DotW8<1>>(a, f, stream);
-  if (M <= kGemvMaxM) return launch_linear_auto<DotW8<2>>(a, f, stream);
   if (M <= 16) return launch_linear_auto<MfmaW8<1>>(a, f, stream);
   return launch_linear_auto<MfmaW8<2>>(a, f, stream);
 }

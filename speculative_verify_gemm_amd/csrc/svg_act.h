@@ -114,11 +114,10 @@ SVG_DEV void act_load_row(const float* x, int K, const int8_t* signs, RowRegs<CP
   }
 }
 
-// Rotate and quantize a row loaded by act_load_row (K <= 4 * NT * CPT); codes
-// and the scale go to `st`.  Every thread of the workgroup must call it.
-template <int CPT, class Store>
-SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* red) {
-  const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
+// Sign flip and butterfly of a row loaded by act_load_row; returns this
+// thread's max |u|.
+template <int CPT>
+SVG_DEV float act_rotate_loaded(RowRegs<CPT>& r) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -126,7 +125,13 @@ SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* re
     fwht32_lane4(r.e[i][0], r.e[i][1], r.e[i][2], r.e[i][3]);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(r.e[i][0]), fabsf(r.e[i][1])), fmaxf(fabsf(r.e[i][2]), fabsf(r.e[i][3]))));
   }
-  amax = wg_max(amax, red);
+  return amax;
+}
+
+// Codes and scale of a rotated row whose max |u| over the row is amax.
+template <int CPT, class Store>
+SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Store& st) {
+  const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
   const float sigma = amax / 127.0f;
   const float rinv = 1.0f / sigma;
   const bool fast = sigma >= 0x1p-125f;
@@ -143,6 +148,54 @@ SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* re
       st.word(c, pack4(q));
     }
   }
+}
+
+// Rotate and quantize a row loaded by act_load_row (K <= 4 * NT * CPT); codes
+// and the scale go to `st`.  Every thread of the workgroup must call it.
+template <int CPT, class Store>
+SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* red) {
+  const float amax = wg_max(act_rotate_loaded<CPT>(r), red);
+  act_store_codes<CPT>(r, K, amax, st);
+}
+
+// Maxima of R values over the workgroup with one LDS round.  red: >= 16 * R.
+template <int R>
+SVG_DEV void wg_max_rows(float (&v)[R], float* red) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v[r] = fmaxf(v[r], __shfl_xor(v[r], off));
+  __syncthreads();  // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[wave * R + r] = v[r];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float m = red[r];
+    for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w * R + r]);
+    v[r] = m;
+  }
+}
+
+// Rows 0..M-1 (M <= R) of X (K values each) rotated and quantized at once into
+// LDS rows `out + r * stride` (words) and scales `scale[r]`: all loads issued
+// together and one reduction for all rows, so the latency is one row's.
+// Needs K <= 4 * NT * CPT; every thread of the workgroup must call it.
+template <int R, int CPT>
+SVG_DEV void act_quant_rows_lds(const float* X, int M, int K, const int8_t* signs, u32* out, int stride,
+                                float* scale, float* red) {
+  RowRegs<CPT> rr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) act_load_row<CPT>(X + (size_t)r * K, r < M ? K : 0, signs, rr[r]);
+  float amax[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) amax[r] = act_rotate_loaded<CPT>(rr[r]);
+  wg_max_rows<R>(amax, red);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r < M) act_store_codes<CPT>(rr[r], K, amax[r], StoreLds{out + r * stride, scale + r});
 }
 
 // Rotate and quantize row `x` (K values, K % 32 == 0); codes and the scale

@@ -46,5 +46,6 @@ inline void svg_w8_storage(int N, int K, size_t* wq_bytes, size_t* scale_bytes) 
 // Compute units of the current device (cached per device id).
 int svg_cu_count();
 
-// Largest M served by the dot-product (GEMV) kernels; larger M use MFMA.
-constexpr int kGemvMaxM = 2;
+// The dot-product (GEMV) kernels serve M = 1 (and M <= 2 for 32-wide groups,
+// which have no MFMA form); larger M use MFMA, whose matrix pipe is otherwise
+// idle, with the rows past M zero.

@@ -161,18 +161,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear(LinArgs a) {
 
 // ------------------------------------------------------ fused activation input
 // The fused kernel takes the fp32 activation rows X of a GEMV-sized call
-// (one or two rows), and every workgroup rotates and quantizes them itself
-// into LDS while its first weight batch is in flight, then reads its
-// activation operands from there: no launch of its own for the quantization
-// and nothing shared between workgroups.  Workgroup 0 also writes xq and
-// x_scale (the values act_rht_quant_i8 gives).  K <= kLdsMaxK.
+// (M <= fused_rows<P>(): the GEMV policies' one or two rows), and every
+// workgroup rotates and quantizes them itself into LDS while its first two
+// weight batches are in flight, then reads its activation operands from
+// there: no launch of its own for the quantization and nothing shared between
+// workgroups.  Workgroup 0 also writes xq and x_scale (the values
+// act_rht_quant_i8 gives).  K <= kLdsMaxK.
 //
-// Larger M is not fused this way: each workgroup would quantize all M rows
-// (M x K values) for itself.  Publishing the rows from a few workgroups to
-// the others inside one launch was measured slower than a separate launch:
-// the publishers' loads of X queue behind the other workgroups' weight
-// stream, and the readers' polls too.
+// The MFMA policies are not fused (measured, M = 2..4, in-launch
+// quantization into LDS cost 6 to 10 us per launch against 4 to 6 us for a
+// launch of its own: the weight stream stalls while every workgroup
+// quantizes).  Publishing the rows from a few workgroups to the others
+// inside one launch was measured slower too: the publishers' loads of X
+// queue behind the other workgroups' weight stream, and the readers' polls.
 constexpr int kLdsMaxK = 12288;
+template <class P>
+constexpr int fused_rows() { return P::kMaxTok <= 2 ? P::kMaxTok : 0; }
 
 struct ActIn {
   const float* X;
@@ -181,11 +185,16 @@ struct ActIn {
 
 template <class P, int WAVES, int CPW, int U>
 __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f) {
-  static_assert(P::kMaxTok <= 2, "fused quantization is for one or two rows");
+  constexpr int R = fused_rows<P>();  // LDS rows
+  static_assert(R > 0, "only the GEMV policies are fused");
+  // row chunks per thread held in registers: enough for every K the resident
+  // shapes of this size take (K <= 4096 with 8 waves, <= 12288 with 12 or
+  // 16); a longer row falls back to one row at a time
+  constexpr int CPT = WAVES >= 16 ? 3 : (WAVES >= 12 ? 4 : 2);
   __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
-  __shared__ float act_red[16];
-  __shared__ __align__(16) u32 xl[P::kMaxTok * kLdsMaxK / 4];
-  __shared__ float xsl[P::kMaxTok];
+  __shared__ float act_red[16 * R];
+  __shared__ __align__(16) u32 xl[R * kLdsMaxK / 4];
+  __shared__ float xsl[R];
   P p;
   p.template init<WAVES>(a, red);
   const int KP = ((a.K + 127) >> 7) * 32;  // words per LDS row: K padded to whole 128-k chunks
@@ -193,10 +202,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
     // zero the padding (rows past M, k past K), quantize the rows.  (Reading
     // the rows before the weights were requested was measured slower: every
     // workgroup's row loads then delay the start of the weight stream.)
-    for (int i = threadIdx.x; i < P::kMaxTok * KP; i += blockDim.x)
+    for (int i = threadIdx.x; i < R * KP; i += blockDim.x)
       if (i / KP >= a.M || (i % KP) * 4 >= a.K) xl[i] = 0u;
-    for (int m = 0; m < a.M; ++m)
-      act_quant_row<4>(f.X + (size_t)m * a.K, a.K, f.signs, StoreLds{xl + m * KP, xsl + m}, act_red);
+    if (a.K <= 4 * CPT * (int)blockDim.x) {
+      act_quant_rows_lds<R, CPT>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
+    } else {
+      for (int m = 0; m < a.M; ++m)
+        act_quant_row<CPT>(f.X + (size_t)m * a.K, a.K, f.signs, StoreLds{xl + m * KP, xsl + m}, act_red);
+    }
     __syncthreads();
     if (blockIdx.x == 0) {  // the call's xq / x_scale outputs
       for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x)
@@ -236,7 +249,7 @@ int spread_grid(int ntiles, int block) {
 template <class P, int WAVES, int CPW, int U>
 hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int ntiles = (a.N + kTileRows - 1) / kTileRows;
-  if constexpr (P::kMaxTok <= 2) {
+  if constexpr (fused_rows<P>() > 0) {
     if (f) {
       constexpr auto kernel = k_linear_fused<P, WAVES, CPW, U>;
       hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream,
@@ -263,7 +276,7 @@ hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 template <class P>
 hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
-  if (f && (P::kMaxTok > 2 || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
+  if (f && (a.M > fused_rows<P>() || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
     hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, const_cast<int8_t*>(a.xq),
                                             const_cast<float*>(a.x_scale), stream);
     if (e != hipSuccess) return e;

@@ -206,7 +206,9 @@ FUSED_CASES += [("w4_z4", 32, 1, 50, 96), ("w4_z4", 32, 5, 50, 96), ("w4_z16", 1
                 ("w4_z16", 64, 16, 300, 4096), ("w4_z16", 64, 1, 64, 12288), ("w4_z16", 64, 32, 40, 320),
                 ("w4_z4", 128, 2, 20, 384)]
 FUSED_CASES += [("w8", 0, M, 37, 384) for M in (1, 2, 16, 32)]
-FUSED_CASES += [("w8", 0, 32, 70, 12288), ("w8", 0, 1, 33, 12288)]
+FUSED_CASES += [("w8", 0, 32, 70, 12288), ("w8", 0, 1, 33, 12288), ("w8", 0, 3, 24, 12288), ("w8", 0, 4, 50, 4096)]
+FUSED_CASES += [("w4_z16", 128, 4, 40, 12288), ("w4_z16", 64, 2, 300, 4096), ("w4_z4", 64, 4, 20, 1024),
+                ("w4_z16", 64, 5, 33, 512)]
 
 
 @pytest.mark.parametrize("fmt,group,M,N,K", FUSED_CASES)
