@@ -125,3 +125,40 @@ def tie_rows(M, K, seed, exp=-3, nudge=False):
     signs = np.where(rng.integers(0, 2, size=K) == 0, 1, -1).astype(np.int8)
     x = O.fwht32(u) * signs.astype(np.float64) / 32.0
     return x.astype(np.float32), signs
+
+
+# the launches of one stack layer as the benchmark issues them: member
+# matrices stacked along N into one storage, and the input space they read
+STACK_LAUNCHES = {"qkv": (("q", "k", "v"), "attn_in"), "o": (("o",), "attn_out"),
+                  "gateup": (("gate", "up"), "mlp_in"), "down": (("down",), "mlp_mid")}
+
+
+def stack_launch(layer, launch, fmt, group):
+    """Device storage of one stacked launch of a stack layer, rotated and
+    quantized member by member into consecutive 16-row tiles (as bench.py
+    builds it).  Returns (w, member weights on the device, signs, space)."""
+    import synth
+    members, space = STACK_LAUNCHES[launch]
+    signs = synth.stack_signs(layer, space)
+    Ws = [synth.stack_weight(layer, m, device=DEV) for m in members]
+    N, K = sum(W.shape[0] for W in Ws), Ws[0].shape[1]
+    wq, ws, wz = svg.empty_weights(N, K, fmt, group)
+    sd = to_dev(signs)
+    r0 = 0
+    for W in Ws:
+        mq, ms, mz = svg.stacked_slices(wq, ws, wz, r0, W.shape[0], K, fmt, group)
+        svg.rht_rotate_weights(W, sd, fmt, group, mq, ms, mz)
+        r0 += W.shape[0]
+    return dict(wq=wq, ws=ws, wz=wz, fmt=fmt, group=group, N=N, K=K), Ws, signs, space
+
+
+def stacked_rows(Ws, rows):
+    """Host copy (fp32) of rows `rows` of the matrices Ws stacked along N."""
+    out, r0 = [], 0
+    for W in Ws:
+        n = W.shape[0]
+        sel = [r - r0 for r in rows if r0 <= r < r0 + n]
+        if sel:
+            out.append(W[torch.tensor(sel, device=W.device)].cpu().numpy())
+        r0 += n
+    return np.concatenate(out, axis=0)

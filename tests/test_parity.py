@@ -301,3 +301,46 @@ def test_fused_in_captured_graph():
         assert np.array_equal(C.host(y1).view(np.uint32), ref1.view(np.uint32)), rep
         assert np.array_equal(C.host(y2).view(np.uint32), ref2.view(np.uint32)), rep
         C.gpu_fused(X1, S1, wa, debug=False)  # eager work in between
+
+
+# ------------------------------------------------- full-size stack launches
+STACK_CASES = [("stack_w4g64", 16, "qkv"), ("stack_w4g64", 16, "down"), ("stack_w4g64", 1, "gateup"),
+               ("stack_w4g64", 1, "down"), ("stack_w8", 32, "qkv"), ("stack_w8", 32, "down"),
+               ("stack_w8", 1, "o"), ("stack_w4g128", 32, "down"), ("stack_w4g128", 32, "gateup"),
+               ("stack_w4g128", 1, "qkv"), ("stack_w4g128", 4, "down"), ("stack_w4g128", 8, "o")]
+
+
+@pytest.mark.parametrize("workload,M,launch", STACK_CASES)
+def test_stack_launch_sampled_rows(workload, M, launch):
+    """One launch of the benchmark's stack at full size, issued as bench.py
+    issues it (stacked members, the fused call), checked on sampled output
+    rows: activation codes and scales bit-exact over the whole row, per-group
+    partial sums bit-exact and y within tolerance for 48 random rows plus the
+    first and last row of every member, against the oracle encoding those
+    rows itself.  A second call without the debug output (the timed kernel
+    instance) gives the same y bit for bit."""
+    spec = synth.WORKLOADS[workload]
+    fmt, group = spec["fmt"], spec["group"]
+    w, Ws, signs, space = C.stack_launch(0, launch, fmt, group)
+    N, K = w["N"], w["K"]
+    C.say(f"stack launch {workload} {launch} M={M} N={N} K={K}")
+    x = synth.stack_acts(workload, 0, space, M)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    y2 = C.gpu_fused(x, signs, w, debug=False)[2]
+    rng = np.random.default_rng(N + K + M)
+    edges, r0 = [], 0
+    for W in Ws:
+        edges += [r0, r0 + W.shape[0] - 1]
+        r0 += W.shape[0]
+    rows = sorted(set(rng.choice(N, 48, replace=False).tolist()) | set(edges))
+    Wr = C.stacked_rows(Ws, rows)
+    if fmt == "w8":
+        y_ref, S_ref, qx, sx = O.linear_w8(x, signs, O.prepare_w8(Wr, signs))
+    else:
+        y_ref, S_ref, qx, sx = O.linear_w4(x, signs, O.prepare_w4(Wr, signs, group))
+    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+    assert np.array_equal(C.host(dbg)[:, rows].astype(np.int64), S_ref)
+    yh = C.host(y)
+    check_y(yh[:, rows], y_ref)
+    assert np.array_equal(C.host(y2).view(np.uint32), yh.view(np.uint32))
