@@ -133,7 +133,11 @@ svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
  *  X        fp32 [M][K] row-major, 16-byte aligned.  M <= 32.
  *  signs    int8 [K] (+/-1), 4-byte aligned; the weights' sign vector.
  *  block    must be 32.
- *  xq       int8 [M][K] codes in [-127, 127], 16-byte aligned.
+ *  xq       M*K int8 codes in [-127, 127], 16-byte aligned, in 32-k slabs:
+ *           the code of (row m, k) is byte ((k / 32) * M + m) * 32 + k % 32,
+ *           i.e. slab s = k / 32 holds the 32 codes of row 0, then row 1, ...
+ *           (for M = 1 this is the row itself).  The linears read 16 rows of
+ *           a 64-k run as two contiguous 512-byte pieces this way.
  *  x_scale  fp32 [M]: (max_k |u| / 127) * 2^-5 (0 for an all-zero row); 4-byte
  *           aligned.
  *
@@ -149,7 +153,8 @@ svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs,
  *  integers and the product runs on the int8 matrix path; "Why batch-one
  *  decoding is memory-bound": each pass streams every weight once.]
  *
- *  xq, x_scale   from act_rht_quant_i8 (xq 16-byte aligned), M in 1..32.
+ *  xq, x_scale   from act_rht_quant_i8 (slab layout, xq 16-byte aligned),
+ *                M in 1..32.
  *  wq, w_scale, w_zero, fmt (SVG_W4_ASYM_Z4 or _Z16), group: the tiled
  *                storage from rht_rotate_weights with the same signs, N rows,
  *                K columns (wq 16-byte, w_scale and fp16 w_zero 4-byte aligned).
@@ -171,7 +176,8 @@ svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
  * [KT "How Uzu optimizes bytes and tokens per pass": Large checkpoints are
  *  8-bit symmetric; both operands are integers.]
  *
- *  xq, x_scale   from act_rht_quant_i8 (xq 16-byte aligned), M in 1..32.
+ *  xq, x_scale   from act_rht_quant_i8 (slab layout, xq 16-byte aligned),
+ *                M in 1..32.
  *  wq            tiled int8 codes from rht_rotate_weights (SVG_W8_SYM),
  *                16-byte aligned; w_scale fp16 bits [N].  K <= 131072 (so
  *                that |S| <= 127^2 K fits int32).

@@ -247,6 +247,19 @@ def pack_w8_codes(q: np.ndarray) -> np.ndarray:
     return a.transpose(0, 2, 3, 1, 4).reshape(-1).copy()
 
 
+def pack_act_codes(qx: np.ndarray) -> np.ndarray:
+    """int8 activation codes qx[M, K] in the library's slab byte order (the
+    pages give no layout): K is cut into slabs of 32 values (one transform
+    block each), slabs in k order, and within a slab the M rows' 32 bytes one
+    after another -- byte (m, k) at ((k // 32) * M + m) * 32 + k % 32.  Same
+    size as [M][K]; for M = 1 it is the row itself.  Returns flat int8."""
+    qx = np.asarray(qx, dtype=np.int8)
+    M, K = qx.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    return qx.reshape(M, K // BLOCK, BLOCK).transpose(1, 0, 2).reshape(-1).copy()
+
+
 # ----------------------------------------------------- integer contraction
 def w4_group_partials(qx: np.ndarray, q: np.ndarray, z: np.ndarray, group: int) -> np.ndarray:
     """S[m, n, j] = sum over k in group j of qx[m, k] * (q[n, k] - z[n, j]),

@@ -105,7 +105,7 @@ SVG_DEV void meta_rsrc(rsrc_t& sr, rsrc_t& zr, const uint16_t* w_scale, const vo
 // Tile and block geometry shared by both policies.
 struct W4Common {
   rsrc_t wr, sr, zr, xr;
-  int lane, wave, waves, r, b, M, N, K, KT, KB, NG;
+  int lane, wave, waves, r, b, M, N, K, KT, KB, NG, ldm, m0;
   u32 lane16;
   const float* x_scale;
   float* y;
@@ -121,7 +121,9 @@ struct W4Common {
     KB = (a.K + kMetaK - 1) / kMetaK;
     wr = make_rsrc(a.wq, (u32)ntiles * (u32)KT * 1024u);
     meta_rsrc<Z4>(sr, zr, a.w_scale, a.w_zero, ntiles, KB, kMetaK / G);
-    xr = make_rsrc(a.xq, (u32)a.M * (u32)a.K);
+    xr = make_rsrc(a.xq, (u32)a.ldm * (u32)a.K);
+    ldm = a.ldm;
+    m0 = a.m0;
     lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
     waves = blockDim.x >> 6;
@@ -136,11 +138,12 @@ struct W4Common {
   SVG_DEV u32 w_off(int t, int j, bool valid) const {
     return (valid && j < KT) ? ((u32)t * (u32)KT + (u32)j) * 1024u + lane16 : kOOB;
   }
-  // Offset of the first 16-k run of activation row m in chunk j (the second
-  // run is 64 bytes on).  Rows past M lie past the buffer and read zeros; k
-  // past K inside another row meets weight code 0 and scale 0.
-  SVG_DEV u32 x_off(int m, int j) const {
-    return j < KT ? (u32)m * (u32)K + (u32)(j * 128 + 16 * b) : kOOB;
+  // Offset of this lane's 16-k run `run` (0: k 16b.., 1: k 64 + 16b..) of
+  // activation row m in chunk j; rows past M and chunks past K read zeros (a
+  // run past K lies past the buffer).  A wave's 16 rows of one run are 1 KiB
+  // in two contiguous pieces (slab layout).
+  SVG_DEV u32 x_off(int m, int j, int run) const {
+    return (j < KT && m < M) ? act_slab_off(m0 + m, j * 128 + run * 64 + 16 * b, ldm) : kOOB;
   }
   // Sum the waves' partials of one output in a fixed order.
   SVG_DEV float wave_sum(const float* buf, int rows, int m, int c) const {
@@ -186,9 +189,8 @@ struct MfmaW4 : W4Common {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int h = 0; h < MH; ++h) {
-        const u32 xo = x_off(h * 16 + r, j0 + c);
-        X.a1[c][h] = bload16(xr, xo);
-        X.a2[c][h] = bload16(xr, xo + 64u);
+        X.a1[c][h] = bload16(xr, x_off(h * 16 + r, j0 + c, 0));
+        X.a2[c][h] = bload16(xr, x_off(h * 16 + r, j0 + c, 1));
       }
   }
 
@@ -314,9 +316,8 @@ struct DotW4 : W4Common {
           X.a1[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(row) : zero;
           X.a2[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(row + 64) : zero;
         } else {
-          const u32 xo = x_off(m, j0 + c);
-          X.a1[c][m] = bload16(xr, xo);
-          X.a2[c][m] = bload16(xr, xo + 64u);
+          X.a1[c][m] = bload16(xr, x_off(m, j0 + c, 0));
+          X.a2[c][m] = bload16(xr, x_off(m, j0 + c, 1));
         }
       }
   }
@@ -425,7 +426,7 @@ hipError_t dispatch_g(const LinArgs& a, const ActIn* f, hipStream_t stream) {
     for (int m0 = 0; m0 < a.M; m0 += 8) {
       LinArgs s = a;
       s.M = (a.M - m0) < 8 ? (a.M - m0) : 8;
-      s.xq = a.xq + (size_t)m0 * a.K;
+      s.m0 = a.m0 + m0;
       s.x_scale = a.x_scale + m0;
       s.y = a.y + (size_t)m0 * a.N;
       s.dbg = DBG ? a.dbg + (size_t)m0 * a.N * NG : nullptr;
@@ -445,7 +446,7 @@ hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
                            float* y, int32_t* dbg, const float* X, const int8_t* signs,
                            hipStream_t stream) {
-  const LinArgs a{xq, x_scale, M, K, wq, w_scale, w_zero, N, y, dbg};
+  const LinArgs a{xq, x_scale, M, K, wq, w_scale, w_zero, N, y, dbg, M, 0};
   const ActIn fa{X, signs};
   const ActIn* f = X ? &fa : nullptr;
 #define SVG_G_CASE(G)                                                                                  \

@@ -31,7 +31,7 @@ namespace {
 // 16b + r holds row r, k in [16b, 16b+16) of the chunk.
 struct W8Common {
   rsrc_t wr, xr;
-  int lane, wave, waves, r, b, M, N, K, KT;
+  int lane, wave, waves, r, b, M, N, K, KT, ldm, m0;
   u32 lane16;
   const float* x_scale;
   const uint16_t* w_scale;
@@ -45,7 +45,9 @@ struct W8Common {
     const int ntiles = (a.N + kTileRows - 1) / kTileRows;
     KT = (a.K + 63) >> 6;
     wr = make_rsrc(a.wq, (u32)ntiles * (u32)KT * 1024u);
-    xr = make_rsrc(a.xq, (u32)a.M * (u32)a.K);
+    xr = make_rsrc(a.xq, (u32)a.ldm * (u32)a.K);
+    ldm = a.ldm;
+    m0 = a.m0;
     lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
     waves = blockDim.x >> 6;
@@ -60,10 +62,11 @@ struct W8Common {
   SVG_DEV u32 w_off(int t, int j, bool valid) const {
     return (valid && j < KT) ? ((u32)t * (u32)KT + (u32)j) * 1024u + lane16 : kOOB;
   }
-  // Activation row m, chunk j: rows past M lie past the buffer (zeros); k
-  // past K inside another row meets weight code 0.
+  // This lane's 16 codes of activation row m in chunk j (k 64j + 16b ..);
+  // rows past M and chunks past K read zeros (slab layout: a wave's 16 rows
+  // are 1 KiB in two contiguous pieces).
   SVG_DEV u32 x_off(int m, int j) const {
-    return j < KT ? (u32)m * (u32)K + (u32)(j * 64 + 16 * b) : kOOB;
+    return (j < KT && m < M) ? act_slab_off(m0 + m, j * 64 + 16 * b, ldm) : kOOB;
   }
   // Sum the waves' partials of one output (exact), scale, store.
   SVG_DEV void store(const int* buf, int rows, int m, int c, int t) const {
@@ -215,7 +218,7 @@ struct MfmaW8 : W8Common {
 hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
                            const int8_t* signs, hipStream_t stream) {
-  const LinArgs a{xq, x_scale, M, K, wq, w_scale, nullptr, N, y, dbg};
+  const LinArgs a{xq, x_scale, M, K, wq, w_scale, nullptr, N, y, dbg, M, 0};
   const ActIn fa{X, signs};
   const ActIn* f = X ? &fa : nullptr;
   if (M <= 1) return launch_linear_auto<DotW8<1>>(a, f, stream);

@@ -68,19 +68,18 @@ SVG_DEV u32 pack4(const int q[4]) {
 }
 
 // Where act_quant_row puts its results: packed code words and the row scale.
-// StoreGlobal<AUX>: global memory through buffer stores with cache policy AUX
-// (0, or kDeviceCoherent when other workgroups of the same launch read the
-// results: the stores then write through to the device's point of coherence
-// instead of staying in this XCD's L2).  StoreLds: a row of LDS words.
-constexpr int kDeviceCoherent = 16;  // sc1: device scope
-
-template <int AUX>
+// StoreGlobal: row m of a global code buffer of ldm rows in 32-k slabs
+// (include/svgemm.h).  StoreLds: a row of LDS words in k order.
 struct StoreGlobal {
   rsrc_t out, sc;
-  SVG_DEV StoreGlobal(int8_t* row, float* scale, int K)
-      : out(make_rsrc(row, (u32)K)), sc(make_rsrc(scale, 4u)) {}
-  SVG_DEV void word(u32 c, u32 v) const { __builtin_amdgcn_raw_buffer_store_b32(v, out, 4u * c, 0u, AUX); }
-  SVG_DEV void scale(float v) const { __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), sc, 0u, 0u, AUX); }
+  u32 m, ldm;
+  SVG_DEV StoreGlobal(int8_t* xq, int m_, int ldm_, float* scale, int K)
+      : out(make_rsrc(xq, (u32)ldm_ * (u32)K)), sc(make_rsrc(scale, 4u)), m((u32)m_), ldm((u32)ldm_) {}
+  // word c holds k = 4c .. 4c + 3: slab c / 8, bytes 4 (c % 8) of the row's 32
+  SVG_DEV void word(u32 c, u32 v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(v, out, ((c >> 3) * ldm + m) * 32u + 4u * (c & 7u), 0u, 0);
+  }
+  SVG_DEV void scale(float v) const { __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), sc, 0u, 0u, 0); }
 };
 
 struct StoreLds {
@@ -90,8 +89,9 @@ struct StoreLds {
   SVG_DEV void scale(float v) const { *sc = v; }
 };
 
-// A row's raw inputs held in registers: chunks threadIdx.x + NT * i, i < CPT
-// (chunks past the row are zeros), and their sign words.
+// A row's raw inputs held in registers: chunks tid + NT * i, i < CPT (chunks
+// past the row are zeros), and their sign words.  tid / NT default to the
+// whole workgroup; a subset of its waves may hold the row instead.
 template <int CPT>
 struct RowRegs {
   float e[CPT][4];
@@ -100,13 +100,13 @@ struct RowRegs {
 
 // Request the loads of row x (K values) into r; nothing is waited for.
 template <int CPT>
-SVG_DEV void act_load_row(const float* x, int K, const int8_t* signs, RowRegs<CPT>& r) {
-  const u32 NT = blockDim.x;
+SVG_DEV void act_load_row(const float* x, int K, const int8_t* signs, RowRegs<CPT>& r,
+                          u32 tid = threadIdx.x, u32 NT = blockDim.x) {
   const rsrc_t xr = make_rsrc(x, (u32)K * 4u);
   const rsrc_t sr = make_rsrc(signs, (u32)K);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const u32 c = threadIdx.x + NT * i;
+    const u32 c = tid + NT * i;
     const u32x4 v = bload16(xr, c * 16u);
     r.sg[i] = (int)bload4(sr, c * 4u);
     r.e[i][0] = __uint_as_float(v[0]); r.e[i][1] = __uint_as_float(v[1]);
@@ -130,15 +130,16 @@ SVG_DEV float act_rotate_loaded(RowRegs<CPT>& r) {
 
 // Codes and scale of a rotated row whose max |u| over the row is amax.
 template <int CPT, class Store>
-SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Store& st) {
-  const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
+SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Store& st,
+                             u32 tid = threadIdx.x, u32 NT = blockDim.x) {
+  const u32 nchunk = (u32)K >> 2;
   const float sigma = amax / 127.0f;
   const float rinv = 1.0f / sigma;
   const bool fast = sigma >= 0x1p-125f;
-  if (threadIdx.x == 0) st.scale(sigma * 0.03125f);  // exact: carries the transform's 2^-5
+  if (tid == 0) st.scale(sigma * 0.03125f);  // exact: carries the transform's 2^-5
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const u32 c = threadIdx.x + NT * i;
+    const u32 c = tid + NT * i;
     if (c < nchunk) {
       int q[4] = {0, 0, 0, 0};
       if (amax > 0.f) {

@@ -39,6 +39,9 @@
 
 constexpr int kTileRows = 16;  // output rows per tile
 
+// xq: activation codes in 32-k slabs (include/svgemm.h): byte (m, k) of a
+// buffer of ldm rows at ((k / 32) * ldm + m) * 32 + k % 32.  A launch covers
+// rows m0 .. m0 + M - 1 of it (x_scale, y and dbg already point at row m0).
 struct LinArgs {
   const int8_t* xq;
   const float* x_scale;
@@ -49,7 +52,13 @@ struct LinArgs {
   int N;
   float* y;
   int32_t* dbg;
+  int ldm, m0;
 };
+
+// Byte offset of the 16 codes k0 .. k0 + 15 (k0 % 16 == 0) of row m.
+SVG_DEV u32 act_slab_off(int m, int k0, int ldm) {
+  return ((u32)(k0 >> 5) * (u32)ldm + (u32)m) * 32u + (u32)(k0 & 31);
+}
 
 // Step Q of a tile: issue the next batch's loads (the tile's batch Q+1, or the
 // first batch of the next tile), then consume batch Q.  `cur` holds batch Q.
@@ -191,6 +200,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   // shapes of this size take (K <= 4096 with 8 waves, <= 12288 with 12 or
   // 16); a longer row falls back to one row at a time
   constexpr int CPT = WAVES >= 16 ? 3 : (WAVES >= 12 ? 4 : 2);
+  // One row (R == 1): only as many leading waves as hold the row with kLoadCPT
+  // chunks per lane request it, before their weights; the other waves request
+  // weights first.  Loads complete in order, so this keeps the row's latency
+  // off the weight stream of most waves and the weights' off the row.
+  constexpr int kLoadCPT = 4;
+  const int nchunk = a.K >> 2;
+  const int LT = min((int)blockDim.x, (nchunk + 64 * kLoadCPT - 1) / (64 * kLoadCPT) * 64);
+  const bool row_early = R == 1 && nchunk <= LT * kLoadCPT;
+  RowRegs<kLoadCPT> early;
   __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
   __shared__ float act_red[16 * R];
   __shared__ __align__(16) u32 xl[R * kLdsMaxK / 4];
@@ -198,13 +216,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   P p;
   p.template init<WAVES>(a, red);
   const int KP = ((a.K + 127) >> 7) * 32;  // words per LDS row: K padded to whole 128-k chunks
-  stream_tiles<P, WAVES, CPW, U, true>(p, a, blockIdx.x, gridDim.x, [] {}, [&] {
-    // zero the padding (rows past M, k past K), quantize the rows.  (Reading
-    // the rows before the weights were requested was measured slower: every
-    // workgroup's row loads then delay the start of the weight stream.)
+  stream_tiles<P, WAVES, CPW, U, true>(p, a, blockIdx.x, gridDim.x, [&] {
+    if (row_early && (int)threadIdx.x < LT) act_load_row<kLoadCPT>(f.X, a.K, f.signs, early, threadIdx.x, LT);
+  }, [&] {
+    // zero the padding (rows past M, k past K), quantize the rows.  (All
+    // waves reading the rows before their weights was measured slower: the
+    // start of the whole weight stream waits for the rows.)
     for (int i = threadIdx.x; i < R * KP; i += blockDim.x)
       if (i / KP >= a.M || (i % KP) * 4 >= a.K) xl[i] = 0u;
-    if (a.K <= 4 * CPT * (int)blockDim.x) {
+    if (row_early) {
+      const bool holds = (int)threadIdx.x < LT;
+      const float amax = wg_max(holds ? act_rotate_loaded<kLoadCPT>(early) : 0.f, act_red);
+      if (holds) act_store_codes<kLoadCPT>(early, a.K, amax, StoreLds{xl, xsl}, threadIdx.x, LT);
+    } else if (a.K <= 4 * CPT * (int)blockDim.x) {
       act_quant_rows_lds<R, CPT>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
     } else {
       for (int m = 0; m < a.M; ++m)
@@ -212,8 +236,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
     }
     __syncthreads();
     if (blockIdx.x == 0) {  // the call's xq / x_scale outputs
-      for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x)
-        reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[i] = xl[(i / (a.K / 4)) * KP + i % (a.K / 4)];
+      for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x) {
+        const int m = i / (a.K / 4), w = i % (a.K / 4);  // word w (k = 4w) of row m
+        reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[((w >> 3) * a.ldm + a.m0 + m) * 8 + (w & 7)] =
+            xl[m * KP + w];
+      }
       if (threadIdx.x < a.M) const_cast<float*>(a.x_scale)[threadIdx.x] = xsl[threadIdx.x];
     }
     p.xlds = reinterpret_cast<const int8_t*>(xl);

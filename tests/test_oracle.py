@@ -312,6 +312,29 @@ def test_w8_tiled_layout_element_by_element(N, K):
     assert np.count_nonzero(p) == np.count_nonzero(q)
 
 
+@pytest.mark.parametrize("M,K", [(1, 64), (3, 96), (16, 256), (32, 32)])
+def test_act_slab_layout_element_by_element(M, K):
+    rng = np.random.default_rng(M * 1000 + K)
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    p = O.pack_act_codes(q)
+    assert p.size == M * K
+    for m in range(M):
+        for k in range(K):
+            assert p[((k // 32) * M + m) * 32 + k % 32] == q[m, k]
+
+
+def test_act_slab_layout_worked_example():
+    # two tokens, K = 64: slab 0 holds token 0's k 0..31 then token 1's k 0..31
+    q = np.arange(128, dtype=np.int64).reshape(2, 64).astype(np.int8)
+    p = O.pack_act_codes(q)
+    assert p[:32].tolist() == list(range(0, 32))
+    assert p[32:64].tolist() == list(range(64, 96))
+    assert p[64:96].tolist() == list(range(32, 64))
+    assert p[96:].tolist() == [v - 256 if v > 127 else v for v in range(96, 128)]
+    one = q[:1]
+    assert np.array_equal(O.pack_act_codes(one), one.reshape(-1))  # one token: the row itself
+
+
 # ------------------------------------------------------- contraction pins
 @pytest.mark.parametrize("group", [32, 64, 128])
 def test_w4_partials_match_brute_force(group):

@@ -1,7 +1,8 @@
 """GPU parity: the HIP library against the CPU oracle, through the C ABI.
 
 Integer stages (activation codes, weight codes, scales and zeros, per-group
-int32 partial sums) must match bit for bit; fp32 outputs must match the fp64
+int32 partial sums) must match bit for bit, in the library's storage orders
+(the oracle's packers give them); fp32 outputs must match the fp64
 reference within 2e-3 (oracle.output_error: elementwise over |y_ref| >= 1e-3
 of the row maximum, and row-normwise over all elements).
 
@@ -53,7 +54,7 @@ def test_act_codes_bit_exact(M, K, src):
             x[1] = 0.0  # an all-zero token
     qx, sx = O.quant_acts(x, signs)
     xq, xs = C.gpu_quant_acts(x, signs)
-    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
 
 
@@ -109,7 +110,7 @@ def test_linear_matches_oracle(fmt, group, M, N, K):
         ow = O.prepare_w4(W, signs, group)
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
     w = C.oracle_weights_to_dev(ow, fmt)
-    y, dbg = C.gpu_linear(C.to_dev(qx), C.to_dev(sx), w)
+    y, dbg = C.gpu_linear(C.to_dev(O.pack_act_codes(qx).reshape(qx.shape)), C.to_dev(sx), w)
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
 
@@ -158,7 +159,7 @@ def test_full_size_single_matrix(src):
     w = C.gpu_prepare(W, signs, fmt, g)
     xq, xs = C.gpu_quant_acts(x, signs)
     y, dbg = C.gpu_linear(xq, xs, w)
-    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(w["wq"]), O.pack_w4_codes(ow["q"]))
     assert np.array_equal(C.host(w["ws"]).view(np.uint16),
                           O.tile_group_params(ow["s"], x.shape[1], g).view(np.uint16))
@@ -191,12 +192,12 @@ def test_act_codes_at_rounding_ties(nudge):
     x, signs = C.tie_rows(M, K, seed=5 + int(nudge), nudge=nudge)
     qx, sx = O.quant_acts(x, signs)
     xq, xs = C.gpu_quant_acts(x, signs)
-    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     _x, W, _s = synth.random_case(1, N, K, seed=77)
     w = C.oracle_weights_to_dev(O.prepare_w4(W, signs, 64), "w4_z16")
     fq, fs, _y, _d = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(fq), qx)
+    assert np.array_equal(C.host(fq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(fs).view(np.uint32), sx.view(np.uint32))
 
 
@@ -226,7 +227,7 @@ def test_fused_matches_oracle(fmt, group, M, N, K):
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
     w = C.oracle_weights_to_dev(ow, fmt)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
@@ -338,7 +339,7 @@ def test_stack_launch_sampled_rows(workload, M, launch):
         y_ref, S_ref, qx, sx = O.linear_w8(x, signs, O.prepare_w8(Wr, signs))
     else:
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, O.prepare_w4(Wr, signs, group))
-    assert np.array_equal(C.host(xq), qx)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     assert np.array_equal(C.host(dbg)[:, rows].astype(np.int64), S_ref)
     yh = C.host(y)
