@@ -242,7 +242,9 @@ hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* 
   else if (nchunk <= 512) SVG_ACT(512, 1);
   else if (nchunk <= 1024) SVG_ACT(1024, 1);
   else if (nchunk <= 2048) SVG_ACT(1024, 2);
+  else if (nchunk <= 3072) SVG_ACT(1024, 3);
   else if (nchunk <= 4096) SVG_ACT(1024, 4);
+  else if (nchunk <= 6144) SVG_ACT(1024, 6);
   else SVG_ACT(1024, 8);  // past 8192 chunks the row is read twice
 #undef SVG_ACT
   return hipGetLastError();

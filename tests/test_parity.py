@@ -40,7 +40,10 @@ def check_y(y, y_ref, tol=TOL):
 
 # ------------------------------------------------------------ activations
 ACT_CASES = [(1, 1024, "single_1k"), (1, 4096, "decode_12k"), (16, 4096, None), (32, 12288, None),
-             (3, 96, None), (5, 1120, None), (2, 32, None), (7, 2080, None)]
+             (3, 96, None), (5, 1120, None), (2, 32, None), (7, 2080, None),
+             # one row length per launch shape of the stand-alone kernel (rows of
+             # 3, 6 and 8 chunks per thread, and a row read twice)
+             (2, 8224, None), (2, 16416, None), (3, 32736, None), (1, 32800, None)]
 
 
 @pytest.mark.parametrize("M,K,src", ACT_CASES)
