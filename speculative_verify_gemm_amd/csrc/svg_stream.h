@@ -298,8 +298,10 @@ hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 // two weight batches in flight, and kFixedRegs for everything else; it must
 // stay within 128 VGPRs (two 8-wave or one 16-wave workgroup per CU, all waves
 // resident), else 192 for an 8-wave or 168 for a 12-wave workgroup alone on
-// its CU.  K ranges that
-// fit no shape take the plain loop.
+// its CU, and last 256 (an 8-wave workgroup alone on its CU, two waves per
+// SIMD: the 16 or 32 token rows of K = 12288 stay resident that way, which
+// halves the launch time against the plain loop).  K ranges that fit no
+// shape take the plain loop.
 template <class P>
 hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
@@ -316,9 +318,12 @@ hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stre
   if (KT <= 16) { SVG_TRY(8, 2, 2, 128); else SVG_TRY(8, 2, 1, 192); }
   if (KT <= 32) { SVG_TRY(8, 4, 4, 128); else SVG_TRY(8, 4, 2, 192); }
   if (KT <= 64) { SVG_TRY(16, 4, 4, 128); else SVG_TRY(16, 4, 2, 128); }
-  if (KT <= 96) { SVG_TRY(16, 6, 2, 128); else SVG_TRY(12, 8, 2, 168); else SVG_TRY(16, 6, 1, 128); }
+  if (KT <= 96) {
+    SVG_TRY(16, 6, 2, 128); else SVG_TRY(12, 8, 2, 168); else SVG_TRY(16, 6, 1, 128);
+    else SVG_TRY(8, 12, 2, 256); else SVG_TRY(8, 12, 1, 256);
+  }
   if (KT <= 128) { SVG_TRY(16, 8, 4, 128); else SVG_TRY(16, 8, 2, 128); }
-  if (KT <= 192) { SVG_TRY(16, 12, 4, 128); else SVG_TRY(16, 12, 2, 128); }
+  if (KT <= 192) { SVG_TRY(16, 12, 4, 128); else SVG_TRY(16, 12, 2, 128); else SVG_TRY(8, 24, 2, 256); }
 #undef SVG_TRY
 #undef SVG_FITS
   return launch_linear<P, 8, 0, 1>(a, f, stream);

@@ -100,6 +100,10 @@ LIN_CASES += [("w4_z4", 32, M, 50, 96) for M in (1, 4, 32)]               # K < 
 LIN_CASES += [("w4_z16", 64, 16, 300, 4096), ("w4_z16", 128, 32, 130, 12288)]
 LIN_CASES += [("w8", 0, M, 37, 384) for M in (1, 2, 3, 16, 17, 32)]
 LIN_CASES += [("w8", 0, M, 29, 96) for M in (1, 32)] + [("w8", 0, 32, 70, 12288)]
+# more than 16 rows with long K: 8-wave workgroups of 256 registers, also
+# with K short of the shape's chunks (the last waves read zeros)
+LIN_CASES += [("w4_z16", 64, 24, 48, 12288), ("w4_z4", 64, 20, 33, 10240), ("w4_z16", 128, 31, 16, 8320),
+              ("w8", 0, 17, 40, 11264), ("w8", 0, 25, 24, 12288)]
 
 
 @pytest.mark.parametrize("fmt,group,M,N,K", LIN_CASES)
