@@ -190,6 +190,50 @@ def random_case(M: int, N: int, K: int, seed: int, w_std: float = W_STD,
     return x, W, signs
 
 
+# ---------------------------------------------------------------- draft trees
+def draft_tree(T: int, V: int, seed: int, shape: str = "bushy", accept: int | None = None,
+               ties: bool = False):
+    """A verified draft tree of T nodes over a V-token vocabulary:
+    (logits[T, V] fp32, parent[T] int32, draft[T] int32).
+
+    Node 0 is the root (parent -1); node i >= 1 hangs under an earlier node:
+    "chain" (parent i - 1), "star" (parent 0) or "bushy" (uniform over the
+    four nodes before it).  Drafted tokens are uniform over the vocabulary.
+    Logits are N(0, 1).  With `accept` = d, the root path of a random node of
+    depth >= d is made to agree for its first d steps (the parent's row gets
+    logit 10 at the child's token) and to disagree at step d + 1 (logit -10),
+    so that the accepted depth is about d (a sibling can still agree by
+    chance).  With `ties`, a few rows get their largest value copied to a
+    random index (an exact fp32 tie, unless that index already held it)."""
+    rng = rng_for("test", seed, 7, "x")
+    parent = np.full(T, -1, dtype=np.int32)
+    for i in range(1, T):
+        if shape == "chain":
+            parent[i] = i - 1
+        elif shape == "star":
+            parent[i] = 0
+        else:
+            parent[i] = rng.integers(max(0, i - 4), i)
+    draft = rng.integers(0, V, size=T).astype(np.int32)
+    logits = rng.standard_normal((T, V), dtype=np.float32)
+    if accept is not None:
+        depth = np.zeros(T, dtype=np.int64)
+        for i in range(1, T):
+            depth[i] = depth[parent[i]] + 1
+        deep = np.flatnonzero(depth >= min(accept, int(depth.max())))
+        node = int(rng.choice(deep))
+        path = [node]
+        while path[-1] != 0:
+            path.append(int(parent[path[-1]]))
+        path = path[::-1]
+        for step, (a, b) in enumerate(zip(path, path[1:])):
+            logits[a, draft[b]] = np.float32(10.0 if step < accept else -10.0)
+    if ties and V > 1:
+        for r in rng.choice(T, size=max(1, T // 4), replace=False):
+            logits[r, int(rng.integers(0, V))] = logits[r].max()
+    return logits, parent, draft
+
+
 # -------------------------------------------------------------- device draws
 def stack_weight(layer: int, name: str, device="cuda"):
     """fp32 W[N, K] of one stack matrix, drawn with torch on `device`:
