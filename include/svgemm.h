@@ -217,6 +217,53 @@ svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* sig
                                  const uint16_t* w_scale, int N, float* y,
                                  int32_t* partials_debug, void* stream);
 
+/*
+ * tree_accept_greedy -- greedy acceptance of a verified draft tree.
+ * [KT "Producing several tokens from one model pass": the main model checks the
+ *  drafted positions together, keeps the valid prefix and continues from the
+ *  first rejected position with its own token -- five drafted tokens of which
+ *  it agrees with the first four advance the sequence by five; "Issue with
+ *  parallel draft generation": over a tree of drafts it accepts the longest
+ *  valid path.  The pages give no procedure beyond that; the readings below
+ *  are this library's.]
+ *
+ *  logits    [T][V] fp32, row-major, 4-byte aligned: row i is the target
+ *            model's prediction for the position after node i (the verify
+ *            pass's output rows, in the order of its batch).
+ *  T         nodes, 1 <= T <= SVG_TREE_MAX_NODES.  Node 0 is the root: the
+ *            last token already in the sequence.
+ *  V         vocabulary size, >= 1.
+ *  parent    [T] int32: parent[0] = -1, and 0 <= parent[i] < i for i >= 1.
+ *  draft     [T] int32: the token of each node (draft[0] is not read).
+ *  target    OUTPUT [T] int32: the target's greedy choice at each node, the
+ *            index of the largest logit of its row, the smallest index among
+ *            equal maxima (NaN logits are outside the contract).
+ *  path      OUTPUT [T] int32: the accepted nodes below the root, root side
+ *            first, then -1.  Node i >= 1 is valid when its parent is valid and
+ *            draft[i] == target[parent[i]] (the root is valid); the accepted
+ *            path is the root path of the deepest valid node, the one with the
+ *            smallest index among equally deep ones.
+ *  emit      OUTPUT [T] int32: the emitted tokens -- the drafted tokens along
+ *            the path, then the target's choice at its last node -- then -1.
+ *  n_emit    OUTPUT [1] int32: the number of emitted tokens (path length + 1);
+ *            -1 if parent[] breaks the rule above, and then path and emit are
+ *            all -1 (the device checks the tree; the host never reads it).
+ *  workspace SVG_TREE_WORKSPACE_BYTES of device memory, 8-byte aligned,
+ *            zero-filled by the caller before its first use; every call leaves
+ *            it zero-filled again.  Calls that may run at the same time must
+ *            use different workspaces.
+ *
+ *  One launch: the logits stream once (T * V * 4 bytes); the workgroup that
+ *  finishes last reads the row maxima and walks the tree.
+ *  Errors: SVG_EINVAL for a null pointer, T < 1 or V < 1; SVG_EUNSUPPORTED for
+ *  T > SVG_TREE_MAX_NODES; SVG_EALIGN for logits not 4-byte or workspace not
+ *  8-byte aligned.
+ */
+enum { SVG_TREE_MAX_NODES = 32, SVG_TREE_WORKSPACE_BYTES = 512 };
+svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* parent,
+                              const int32_t* draft, int32_t* target, int32_t* path, int32_t* emit,
+                              int32_t* n_emit, void* workspace, void* stream);
+
 /* Text of the last error on the calling thread ("" after a successful call);
  * valid until the next call on this thread. */
 const char* svg_last_error(void);

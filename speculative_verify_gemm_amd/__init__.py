@@ -43,8 +43,9 @@ def _load():
     lib.w8a8_linear.argtypes = [vp, vp, i, i, vp, vp, i, vp, vp, vp]
     lib.act_quant_w4a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.act_quant_w8a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, i, vp, vp, vp]
+    lib.tree_accept_greedy.argtypes = [vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
     for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear,
-               lib.act_quant_w4a8_linear, lib.act_quant_w8a8_linear):
+               lib.act_quant_w4a8_linear, lib.act_quant_w8a8_linear, lib.tree_accept_greedy):
         fn.restype = ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.svg_weight_sizes.argtypes = [i, i, i, i, u64p, u64p, u64p]
@@ -233,6 +234,34 @@ def act_quant_w8a8_linear(X, signs, xq, x_scale, wq, w_scale, N, y, partials_deb
 
 
 # ------------------------------------------------------------- allocation
+
+TREE_MAX_NODES, TREE_WORKSPACE_BYTES = 32, 512
+
+
+def tree_workspace(device="cuda"):
+    """A zero-filled workspace for tree_accept_greedy (each call leaves it
+    zero-filled; calls that may overlap need workspaces of their own)."""
+    return torch.zeros(TREE_WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+
+
+def tree_accept_greedy(logits, parent, draft, target, path, emit, n_emit, workspace, stream=None):
+    """Greedy acceptance of a verified draft tree (include/svgemm.h): logits
+    [T, V] fp32; parent, draft [T] int32; outputs target, path, emit [T] and
+    n_emit [1] int32; workspace from tree_workspace()."""
+    _dev(logits, "logits", torch.float32)
+    T, V = logits.shape
+    for name, t in (("parent", parent), ("draft", draft), ("target", target), ("path", path),
+                    ("emit", emit)):
+        _dev(t, name, torch.int32)
+        if tuple(t.shape) != (T,):
+            raise ValueError(f"{name} must have shape [{T}]")
+    _dev(n_emit, "n_emit", torch.int32)
+    _dev(workspace, "workspace", torch.uint8)
+    if n_emit.numel() < 1 or workspace.numel() < TREE_WORKSPACE_BYTES:
+        raise ValueError("n_emit needs 1 element and workspace TREE_WORKSPACE_BYTES bytes")
+    _check(lib.tree_accept_greedy(_p(logits), T, V, _p(parent), _p(draft), _p(target), _p(path),
+                                  _p(emit), _p(n_emit), _p(workspace), _stream(stream, logits)))
+
 
 def empty_weights(N, K, fmt, group, device="cuda"):
     """Uninitialised tiled storage for rht_rotate_weights: flat (wq, w_scale,

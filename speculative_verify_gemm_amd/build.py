@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsvgemm.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["rht_quant.hip", "linear_w4.hip", "linear_w8.hip", "svgemm.hip"]
+SOURCES = ["rht_quant.hip", "linear_w4.hip", "linear_w8.hip", "tree_accept.hip", "svgemm.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

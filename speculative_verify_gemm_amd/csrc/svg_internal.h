@@ -24,6 +24,12 @@ hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
                            const int8_t* signs, hipStream_t stream);
 
+// Greedy acceptance of a draft tree (tree_accept.hip); `workspace` is the
+// caller's zero-filled SVG_TREE_WORKSPACE_BYTES, left zero-filled.
+hipError_t svg_launch_tree_accept(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,
+                                  int32_t* target, int32_t* path, int32_t* emit, int32_t* n_emit, void* workspace,
+                                  hipStream_t stream);
+
 // Bytes of the weight storage (include/svgemm.h describes the layout).
 // W4 codes: tiled, rows padded to 16 and K to 128.  Scales and zeros:
 // blocked per (16-row tile, 512-k block, row), rows padded to 16 and K to

@@ -225,4 +225,18 @@ svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* sig
   return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, X, signs, s));
 }
 
+svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,
+                              int32_t* target, int32_t* path, int32_t* emit, int32_t* n_emit, void* workspace,
+                              void* stream) {
+  static const char* fn = "tree_accept_greedy";
+  if (!logits || !parent || !draft || !target || !path || !emit || !n_emit || !workspace)
+    return fail(SVG_EINVAL, fn, "null pointer");
+  if (T < 1 || V < 1) return fail(SVG_EINVAL, fn, "T and V must be >= 1");
+  if (T > SVG_TREE_MAX_NODES) return fail(SVG_EUNSUPPORTED, fn, "T > SVG_TREE_MAX_NODES");
+  if (!aligned(logits, 4)) return fail(SVG_EALIGN, fn, "logits must be 4-byte aligned");
+  if (!aligned(workspace, 8)) return fail(SVG_EALIGN, fn, "workspace must be 8-byte aligned");
+  return hip_status(fn, svg_launch_tree_accept(logits, T, V, parent, draft, target, path, emit, n_emit, workspace,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -30,7 +30,7 @@ def svg():
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
         ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
-         "svg_last_error", "svg_weight_sizes", "w4a8_linear", "w8a8_linear"])
+         "svg_last_error", "svg_weight_sizes", "tree_accept_greedy", "w4a8_linear", "w8a8_linear"])
 
 
 def test_library_exports_every_declared_symbol(svg):
@@ -167,3 +167,22 @@ def test_binding_has_no_cpu_path(svg):
     with pytest.raises(ValueError):
         svg.act_rht_quant_i8(x, torch.ones(64, dtype=torch.int8), torch.zeros((1, 64), dtype=torch.int8),
                              torch.zeros(1))
+
+
+def _tree(svg, **kw):
+    args = dict(logits=A, T=4, V=100, parent=A, draft=A, target=A, path=A, emit=A, n=A, ws=A)
+    args.update(kw)
+    return svg.lib.tree_accept_greedy(args["logits"], args["T"], args["V"], args["parent"], args["draft"],
+                                      args["target"], args["path"], args["emit"], args["n"], args["ws"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=NULL), 1), (dict(parent=NULL), 1), (dict(draft=NULL), 1), (dict(target=NULL), 1),
+    (dict(path=NULL), 1), (dict(emit=NULL), 1), (dict(n=NULL), 1), (dict(ws=NULL), 1),
+    (dict(T=0), 1), (dict(V=0), 1), (dict(T=-2), 1),
+    (dict(T=33), 2),
+    (dict(logits=MIS), 3), (dict(ws=ctypes.c_void_p(0x10004)), 3),
+])
+def test_tree_accept_validation(svg, kw, code):
+    assert _tree(svg, **kw) == code
+    assert svg.last_error().startswith("tree_accept_greedy:")
