@@ -323,6 +323,53 @@ def cpu_baseline(stack, M, min_seconds=12.0, max_reps=32):
                 seconds=dt, cpu=platform.processor() or platform.machine())
 
 
+def time_tree_accept(torch, dev, T, V, reps=50):
+    """Greedy acceptance of a T-node draft tree over V logits per node (the
+    step that follows a verify pass): mean time per call of back-to-back
+    tree_accept_greedy calls on one stream (each depends on the previous one
+    through the shared workspace), captured in a HIP graph so the host's
+    enqueue rate does not bound them."""
+    import numpy as np
+    import synth
+    import speculative_verify_gemm_amd as svg
+    logits, parent, draft = synth.draft_tree(T, V, seed=2026, shape="bushy", accept=T // 2, ties=True)
+    lg = torch.from_numpy(logits).to(dev)
+    pa = torch.from_numpy(parent.astype(np.int32)).to(dev)
+    dr = torch.from_numpy(draft.astype(np.int32)).to(dev)
+    outs = [torch.empty(T, dtype=torch.int32, device=dev) for _ in range(3)]
+    n = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = svg.tree_workspace(dev)
+
+    def call():
+        svg.tree_accept_greedy(lg, pa, dr, outs[0], outs[1], outs[2], n, ws)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(5):
+            call()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            call()
+    g.replay()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / (4 * reps)
+    nbytes = T * V * 4
+    return dict(T=T, V=V, us_per_call=round(us, 3), bytes_per_call=nbytes,
+                GB_per_s=round(nbytes / (us * 1e-6) / 1e9, 2),
+                frac_of_hbm_peak=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                emitted_tokens=int(n.cpu()[0])), (logits, parent, draft)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +383,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the M=1 comparison pass")
     ap.add_argument("--sweep", default=None, help="comma-separated M values: report a pass per M")
+    ap.add_argument("--tree-vocab", type=int, default=131072,
+                    help="logits per node of the draft-tree acceptance measured after the pass (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first copy this many MiB device to device (three times): the copy of known "
                          "size that scales the HBM byte counters of a profiling run")
@@ -436,10 +485,24 @@ def main():
                          "bytes_per_pass": nbm})
             del gm
         out["sweep"] = rows
+    tree_inputs = None
+    if args.tree_vocab:
+        tree, tree_inputs = time_tree_accept(torch, dev, min(M, 32), args.tree_vocab)
+        print(f"[bench] tree acceptance T={tree['T']} V={tree['V']}: {tree['us_per_call']:.2f} us/call, "
+              f"{tree['GB_per_s']:.1f} GB/s", file=sys.stderr, flush=True)
+        out["tree_accept"] = tree
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
         cb = cpu_baseline(stack, M)
         out["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
+        if tree_inputs is not None:
+            from oracle import tree_oracle as TO
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 1.0:
+                TO.verify_tree(*tree_inputs)
+                reps += 1
+            out["tree_accept"]["cpu_oracle_us_per_call"] = round((time.perf_counter() - t0) / reps * 1e6, 1)
     print(json.dumps(out), flush=True)
 
 

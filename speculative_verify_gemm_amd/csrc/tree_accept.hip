@@ -18,12 +18,13 @@
 //     (order-preserving bits of the value) << 32 | (2^32 - 1 - index), so that
 //     the largest key is the largest value and, among equal values, the
 //     smallest index; it folds the key into its row's slot of the workspace
-//     with a 64-bit atomic max, then counts itself in with an atomic add.
-//  2. The workgroup whose count completes the grid reads the row keys (every
-//     other workgroup has folded its key before counting itself: release and
-//     acquire order at device scope), clears the workspace for the next call,
-//     and walks the tree (at most 32 nodes, one thread: nodes only depend on
-//     earlier nodes).
+//     with a 64-bit atomic max, then counts itself in its row (the workgroup
+//     completing a row counts the row in).
+//  2. The workgroup completing the last row reads the row keys (every
+//     workgroup's key was acknowledged before it counted itself), clears the
+//     workspace for the next call, and walks the tree with one lane per node
+//     (at most 32): pointer jumping over the parent links gives every node's
+//     depth and whether its whole root path agrees.
 // Nothing waits for another workgroup, so no launch order or residency is
 // assumed.
 #include <algorithm>
@@ -34,7 +35,8 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxNodes = 32;
+constexpr int kMaxNodes = 32;  // one lane per node in the walk, bit room in its sort key
+static_assert(kMaxNodes <= 64 && kMaxNodes <= 255, "nodes must fit a wave and the 8-bit index field");
 constexpr int kUnroll = 8;  // float4 loads in flight per thread
 
 typedef unsigned long long u64;
@@ -58,11 +60,9 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept(const float* __restric
                                                          int L, const int32_t* __restrict__ parent,
                                                          const int32_t* __restrict__ draft, int32_t* target,
                                                          int32_t* path, int32_t* emit, int32_t* n_emit,
-                                                         u64* keys, u32* arrivals) {
+                                                         u64* keys, u32* row_count, u32* rows_done) {
   __shared__ u64 wave_best[kThreads / 64];
   __shared__ int last;
-  __shared__ int par[kMaxNodes], tok[kMaxNodes], tgt[kMaxNodes], route[kMaxNodes], depth[kMaxNodes];
-  __shared__ int best_node, depth_best, bad;
 
   // ---- 1. slice maximum
   const int row = blockIdx.x / S, s = blockIdx.x % S;
@@ -103,61 +103,79 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept(const float* __restric
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = umax64(b, wave_best[w]);
     __hip_atomic_fetch_max(keys + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // release: the key above is folded before the count; acquire: the last
-    // workgroup sees every key folded before the counts it read
-    const u32 before = __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = before == gridDim.x - 1;
+    // The key is performed at the device's coherence point before this
+    // workgroup counts itself: wait for its acknowledgement (no cache-wide
+    // write-back is needed, nothing else was written).  The count goes to the
+    // row first, and only the workgroup completing a row counts the row in,
+    // so no single word takes every workgroup's atomic.
+    __builtin_amdgcn_s_waitcnt(0);
+    int done = 0;
+    if (__hip_atomic_fetch_add(row_count + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (u32)S - 1)
+      done = __hip_atomic_fetch_add(rows_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (u32)T - 1;
+    last = done;
   }
   __syncthreads();
   if (!last) return;
 
-  // ---- 2. the last workgroup: choices, reset, tree walk
-  const int t = threadIdx.x;
-  if (t < T) {
-    const u64 key = __hip_atomic_load(keys + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int c = (int)(0xFFFFFFFFu - (u32)key);
-    target[t] = c;
-    tgt[t] = c;
-    par[t] = parent[t];
-    tok[t] = draft[t];
-    __hip_atomic_store(keys + t, (u64)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- 2. the last workgroup, one wave, lane i = node i: choices, reset,
+  // tree walk.  Its loads are issued after the counts it read returned, and
+  // device-scope atomic loads bypass the XCD's cache, so they see every
+  // folded key.
+  if (threadIdx.x >= 64) return;
+  const int i = threadIdx.x;
+  const bool node = i < T;
+  int p = -1, tk = 0, c = 0;
+  if (node) {
+    const u64 key = __hip_atomic_load(keys + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    p = parent[i];
+    tk = draft[i];
+    c = (int)(0xFFFFFFFFu - (u32)key);
+    target[i] = c;
+    __hip_atomic_store(keys + i, (u64)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(row_count + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (t == 0) __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (t == 0) {
-    int b = par[0] != -1;
-    for (int i = 1; i < T; ++i) b |= !(par[i] >= 0 && par[i] < i);
-    bad = b;
-    if (!b) {
-      // valid[i] / depth[i] only depend on the parent, an earlier node
-      unsigned valid = 1u;  // bit i: node i valid (T <= 32)
-      depth[0] = 0;
-      int bn = 0, bd = 0;
-      for (int i = 1; i < T; ++i) {
-        const int p = par[i];
-        depth[i] = depth[p] + 1;
-        if (((valid >> p) & 1u) && tok[i] == tgt[p]) {
-          valid |= 1u << i;
-          if (depth[i] > bd) { bn = i; bd = depth[i]; }
-        }
-      }
-      for (int k = bd - 1, n = bn; k >= 0; --k, n = par[n]) route[k] = n;
-      best_node = bn;
-      depth_best = bd;
+  if (i == 0) __hip_atomic_store(rows_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool bad = __any(node && (i == 0 ? p != -1 : (p < 0 || p >= i)));
+  if (bad) {
+    if (node) { path[i] = -1; emit[i] = -1; }
+    if (i == 0) *n_emit = -1;
+    return;
+  }
+  // Node i's own edge agrees when its token is the parent's choice; it is
+  // valid when every edge of its root path agrees.  Pointer jumping over the
+  // parent links: after ceil(log2 T) rounds every node has folded its whole
+  // root path (ancestor -1 = done): `ok` = all edges agree, `depth` = edges.
+  int anc = p;
+  const int c_parent = __shfl(c, p < 0 ? 0 : p);  // every lane takes part in each exchange
+  int ok = node && (i == 0 || tk == c_parent);
+  int depth = i > 0 && node;
+  for (int step = 1; step < T; step <<= 1) {
+    const int a = anc < 0 ? i : anc;
+    const int ok_a = __shfl(ok, a), depth_a = __shfl(depth, a), anc_a = __shfl(anc, a);
+    if (anc >= 0) {
+      ok = ok && ok_a;
+      depth += depth_a;
+      anc = anc_a;
     }
   }
-  __syncthreads();
-  if (t < T) {
-    if (bad) {
-      path[t] = -1;
-      emit[t] = -1;
-    } else {
-      const int d = depth_best;
-      path[t] = t < d ? route[t] : -1;
-      emit[t] = t < d ? tok[route[t]] : (t == d ? tgt[best_node] : -1);
-    }
+  // deepest valid node, the smallest index among equally deep ones
+  int best_key = (node && ok) ? (depth << 8) | (255 - i) : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) best_key = max(best_key, __shfl_xor(best_key, m));
+  const int bn = 255 - (best_key & 255), d = best_key >> 8;
+  // the path, root side first: lane k holds the node at depth k + 1
+  int on_path = -1;
+  for (int k = d - 1, n = bn; k >= 0; --k) {
+    if (i == k) on_path = n;
+    n = __shfl(p, n);
   }
-  if (t == 0) *n_emit = bad ? -1 : depth_best + 1;
+  const int tok_on_path = __shfl(tk, on_path < 0 ? 0 : on_path);
+  const int bonus = __shfl(c, bn);
+  if (node) {
+    path[i] = i < d ? on_path : -1;
+    emit[i] = i < d ? tok_on_path : (i == d ? bonus : -1);
+  }
+  if (i == 0) *n_emit = d + 1;
 }
 
 }  // namespace
@@ -171,14 +189,17 @@ hipError_t svg_launch_tree_accept(const float* logits, int T, int V, const int32
   const int by_grid = std::max(1, 2 * svg_cu_count() / T);
   const int S = std::max(1, std::min(by_size, by_grid));
   const int L = ((V + S - 1) / S + 3) / 4 * 4;  // values per slice, a multiple of 4
+  // workspace: row keys (u64) at byte 0, per-row counts (u32) at 256, the
+  // count of completed rows at 384
   u64* keys = static_cast<u64*>(workspace);
-  u32* arrivals = reinterpret_cast<u32*>(static_cast<char*>(workspace) + 256);
+  u32* row_count = reinterpret_cast<u32*>(static_cast<char*>(workspace) + 256);
+  u32* rows_done = reinterpret_cast<u32*>(static_cast<char*>(workspace) + 384);
   const bool vec4 = V % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
   if (vec4)
     hipLaunchKernelGGL(k_tree_accept<true>, dim3(T * S), dim3(kThreads), 0, stream, logits, T, V, S, L, parent,
-                       draft, target, path, emit, n_emit, keys, arrivals);
+                       draft, target, path, emit, n_emit, keys, row_count, rows_done);
   else
     hipLaunchKernelGGL(k_tree_accept<false>, dim3(T * S), dim3(kThreads), 0, stream, logits, T, V, S, L, parent,
-                       draft, target, path, emit, n_emit, keys, arrivals);
+                       draft, target, path, emit, n_emit, keys, row_count, rows_done);
   return hipGetLastError();
 }

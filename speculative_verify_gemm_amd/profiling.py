@@ -79,13 +79,15 @@ def _first_arg(inner):
     return inner.rstrip(">")
 
 
-def trace_summary(d, cmd):
+def trace_summary(d, cmd, only=None):
+    """Per-kernel span statistics of a kernel trace; `only`: keep the kernels
+    whose name starts with it (the others are counted as other kernels)."""
     rows = _rows(d, "kernel_trace.csv")
     by, other = {}, []
     for r in rows:
         n = _short(r["Kernel_Name"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if not n.startswith("k_"):
+        if not n.startswith(only or "k_"):
             other.append(dur)
             continue
         wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
@@ -107,8 +109,8 @@ def trace_summary(d, cmd):
             lines.append(f"- `{pol}`: {len(v)} dispatches, mean {statistics.mean(v):.3f} us, "
                          f"median {statistics.median(v):.3f} us")
     if other:
-        lines += ["", f"Other kernels (torch weight generation and fills at set-up): {len(other)} dispatches, "
-                      f"{sum(other) / 1e3:.1f} ms in total."]
+        what = "every other kernel of the run" if only else "torch weight generation and fills at set-up"
+        lines += ["", f"Other kernels ({what}): {len(other)} dispatches, {sum(other) / 1e3:.1f} ms in total."]
     return "\n".join(lines) + "\n"
 
 
@@ -178,6 +180,7 @@ def main(argv=None):
     t.add_argument("dir")
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--only", default=None, help="keep the kernels whose name starts with this")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
@@ -190,7 +193,7 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.what == "trace":
-        text = trace_summary(a.dir, a.cmd)
+        text = trace_summary(a.dir, a.cmd, a.only)
     else:
         text = traffic_summary(a.fetch_dir, a.write_dir, a.calib_mib, a.workload, a.m, a.cmd,
                                a.fetch_json, a.write_json)
