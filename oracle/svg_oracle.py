@@ -29,6 +29,11 @@ What the pages fix, and the readings taken where they are silent:
   symmetric int8 activations with codes in [-127, 127]; min/max asymmetric W4
   per group along K with the range widened to contain 0, fp16 scale, integer
   zero point in [0, 15]; per-output-row symmetric W8 with fp16 scale.
+* A second transform block, 64 (the width of one CDNA wave, where the pages'
+  32 is the width of the SIMD group of the hardware they target), is a
+  variant: the same butterfly with one more stage (h = 32) and the combined
+  overall scale 1/64 folded into the activation scale.  Block and group stay
+  independent.
 * Where floating point decides an integer code, the decision is taken in fp32
   (the kernels' precision) with IEEE division and round-half-to-even, so the
   codes are unique.  The reference output is then formed in fp64 from exact
@@ -46,41 +51,57 @@ F32 = np.float32
 
 
 # ------------------------------------------------------------ the transform
-def hadamard32() -> np.ndarray:
-    """H[i, j] = (-1)^popcount(i & j), i, j in 0..31: the Sylvester-ordered
-    Hadamard matrix of order 32, entries +/-1 [KT "How Uzu optimizes bytes and
-    tokens per pass": a Hadamard matrix holds only +1 and -1 plus one overall
-    scale]."""
-    i = np.arange(BLOCK)
+BLOCKS = (32, 64)  # 32: the pages' block; 64: the wave-wide variant (one CDNA wave)
+
+
+def hadamard(block: int = BLOCK) -> np.ndarray:
+    """H[i, j] = (-1)^popcount(i & j), i, j in 0..block-1: the Sylvester-ordered
+    Hadamard matrix, entries +/-1 [KT "How Uzu optimizes bytes and tokens per
+    pass": a Hadamard matrix holds only +1 and -1 plus one overall scale]."""
+    i = np.arange(block)
     pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
     return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
 
 
-def fwht32(v: np.ndarray) -> np.ndarray:
-    """Unnormalised Walsh-Hadamard transform of every aligned block of 32
+def hadamard32() -> np.ndarray:
+    """The order-32 matrix of the pages' block size."""
+    return hadamard(32)
+
+
+def fwht(v: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform of every aligned block of `block`
     values along the last axis, in v's dtype (fp32 or fp64).
 
-    Stage order h = 1, 2, 4, 8, 16; at stage h every index i of a block with
-    (i & h) == 0 maps the pair (v[i], v[i+h]) to (v[i] + v[i+h], v[i] - v[i+h]),
-    each a single rounded operation.  In exact arithmetic the result is
-    H @ block with H = hadamard32() [KT "How Uzu optimizes bytes and tokens per
-    pass": each block of 32 values is mixed on its own]."""
+    Stage order h = 1, 2, 4, ..., block/2; at stage h every index i of a block
+    with (i & h) == 0 maps the pair (v[i], v[i+h]) to (v[i] + v[i+h],
+    v[i] - v[i+h]), each a single rounded operation.  In exact arithmetic the
+    result is H @ block with H = hadamard(block) [KT "How Uzu optimizes bytes
+    and tokens per pass": each block is mixed on its own]."""
+    if block not in BLOCKS:
+        raise ValueError(f"block must be one of {BLOCKS}")
     v = np.array(v, copy=True)
     shape = v.shape
-    if shape[-1] % BLOCK:
-        raise ValueError("last axis must be a multiple of 32")
-    b = v.reshape(-1, shape[-1] // BLOCK, BLOCK)
-    for h in (1, 2, 4, 8, 16):
-        lo = [i for i in range(BLOCK) if not i & h]
+    if shape[-1] % block:
+        raise ValueError(f"last axis must be a multiple of {block}")
+    b = v.reshape(-1, shape[-1] // block, block)
+    h = 1
+    while h < block:
+        lo = [i for i in range(block) if not i & h]
         hi = [i + h for i in lo]
         a = b[:, :, lo]
         c = b[:, :, hi]
         b[:, :, lo] = a + c
         b[:, :, hi] = a - c
+        h *= 2
     return b.reshape(shape)
 
 
-def rht(r: np.ndarray, signs: np.ndarray, dtype=F32) -> np.ndarray:
+def fwht32(v: np.ndarray) -> np.ndarray:
+    """The transform with the pages' block of 32 (stages h = 1, 2, 4, 8, 16)."""
+    return fwht(v, 32)
+
+
+def rht(r: np.ndarray, signs: np.ndarray, dtype=F32, block: int = BLOCK) -> np.ndarray:
     """Block-diagonal random Hadamard transform of the rows of r along the last
     axis: the +/-1 sign flip first, then the block Hadamard
     [KT "How Uzu optimizes bytes and tokens per pass": random sign flips are
@@ -89,26 +110,27 @@ def rht(r: np.ndarray, signs: np.ndarray, dtype=F32) -> np.ndarray:
     s = np.asarray(signs).astype(dtype)
     if r.shape[-1] != s.shape[-1]:
         raise ValueError("signs length must equal K")
-    return fwht32(r * s)
+    return fwht32(r * s) if block == 32 else fwht(r * s, block)
 
 
 # ------------------------------------------------- activation quantization
-def act_quant_i8(u: np.ndarray):
+def act_quant_i8(u: np.ndarray, block: int = BLOCK):
     """Per-token symmetric int8 quantization of rotated activation rows u[M, K]
     (fp32) [KT "How Uzu optimizes bytes and tokens per pass": activations are
     quantized to 8 bits on the fly].
 
     amax = max_k |u|; sigma = amax / 127 (fp32); q = clamp(rint(u / sigma),
     -127, 127); a zero row gives q = 0.  Returns (q int8 [M, K], scale fp32 [M])
-    where scale = sigma * 2^-5 also carries the transform's overall scale, so
-    that x . w  ~=  scale[m] * sum_k q[m, k] * (dequantized rotated weight)."""
+    where scale = sigma / block also carries the transform's overall scale
+    (1/sqrt(block) on each operand; 2^-5 for the pages' 32), so that
+    x . w  ~=  scale[m] * sum_k q[m, k] * (dequantized rotated weight)."""
     u = np.asarray(u, dtype=F32)
     amax = np.max(np.abs(u), axis=-1)
     sigma = amax / F32(127)
     safe = np.where(amax > 0, sigma, F32(1))
     q = np.clip(np.rint(u / safe[..., None]), -127, 127)
     q = np.where(amax[..., None] > 0, q, F32(0)).astype(np.int8)
-    scale = (sigma * F32(2.0 ** -5)).astype(F32)
+    scale = (sigma * F32(1.0 / block)).astype(F32)  # exact: block is a power of two
     return q, scale
 
 
@@ -291,35 +313,36 @@ def w8a8_output(x_scale: np.ndarray, S: np.ndarray, s: np.ndarray) -> np.ndarray
 
 
 # ------------------------------------------------------------ whole layer
-def prepare_w4(W: np.ndarray, signs: np.ndarray, group: int) -> dict:
+def prepare_w4(W: np.ndarray, signs: np.ndarray, group: int, block: int = BLOCK) -> dict:
     """Offline: rotate the fp32 weight rows, then quantize them as Medium."""
-    u = rht(W, signs, F32)
+    u = rht(W, signs, F32, block)
     q, s, z = quant_w4(u, group)
-    return dict(q=q, s=s, z=z, group=group)
+    return dict(q=q, s=s, z=z, group=group, block=block)
 
 
-def prepare_w8(W: np.ndarray, signs: np.ndarray) -> dict:
+def prepare_w8(W: np.ndarray, signs: np.ndarray, block: int = BLOCK) -> dict:
     """Offline: rotate the fp32 weight rows, then quantize them as Large."""
-    q, s = quant_w8(rht(W, signs, F32))
-    return dict(q=q, s=s)
+    q, s = quant_w8(rht(W, signs, F32, block))
+    return dict(q=q, s=s, block=block)
 
 
-def quant_acts(x: np.ndarray, signs: np.ndarray):
+def quant_acts(x: np.ndarray, signs: np.ndarray, block: int = BLOCK):
     """Online: rotate the activation rows with the weights' signs, then
     quantize them per token to int8."""
-    return act_quant_i8(rht(x, signs, F32))
+    return act_quant_i8(rht(x, signs, F32, block), block)
 
 
 def linear_w4(x: np.ndarray, signs: np.ndarray, w: dict):
-    """One W4A8 linear: returns (y fp64 [M, N], S int64 [M, N, G], qx, x_scale)."""
-    qx, sx = quant_acts(x, signs)
+    """One W4A8 linear: returns (y fp64 [M, N], S int64 [M, N, G], qx, x_scale).
+    The activations take the weights' transform block."""
+    qx, sx = quant_acts(x, signs, w.get("block", BLOCK))
     S = w4_group_partials(qx, w["q"], w["z"], w["group"])
     return w4a8_output(sx, S, w["s"]), S, qx, sx
 
 
 def linear_w8(x: np.ndarray, signs: np.ndarray, w: dict):
     """One W8A8 linear: returns (y fp64 [M, N], S int64 [M, N], qx, x_scale)."""
-    qx, sx = quant_acts(x, signs)
+    qx, sx = quant_acts(x, signs, w.get("block", BLOCK))
     S = w8_partials(qx, w["q"])
     return w8a8_output(sx, S, w["s"]), S, qx, sx
 

@@ -104,6 +104,83 @@ def test_rotation_exact_inverse_on_fractions():
     assert np.max(np.abs(uo - np.array([float(v) for v in u]))) < 1e-9
 
 
+# ------------------------------------------- the wave-wide block (64) pins
+def test_hadamard64_is_sylvester_and_orthogonal():
+    H = O.hadamard(64)
+    assert np.array_equal(H, np.array(brute.sylvester(64), dtype=np.int64))
+    assert np.array_equal(H @ H.T, 64 * np.eye(64, dtype=np.int64))
+    # the order-64 matrix is [[H32, H32], [H32, -H32]] (Sylvester doubling)
+    H32 = O.hadamard32()
+    assert np.array_equal(H, np.block([[H32, H32], [H32, -H32]]))
+
+
+def test_fwht64_of_unit_vectors_gives_columns():
+    U = O.fwht(np.eye(64, dtype=np.float32), 64)
+    assert np.array_equal(U.T.astype(np.int64), np.array(brute.sylvester(64), dtype=np.int64))
+
+
+@pytest.mark.parametrize("K", [64, 192])
+def test_rotation64_matches_explicit_product_on_integers(K):
+    rng = np.random.default_rng(K + 1)
+    x = rng.integers(-1024, 1025, size=(3, K))
+    s = synth.rademacher(K, rng)
+    u = O.rht(x.astype(np.float32), s, np.float32, 64)
+    for r in range(3):
+        ref = brute.rotate_row([int(v) for v in x[r]], [int(v) for v in s], block=64)
+        assert np.array_equal(u[r].astype(np.int64), np.array(ref, dtype=np.int64))
+
+
+def test_rotation64_exactly_reversible_and_product_preserved():
+    rng = np.random.default_rng(17)
+    K = 512
+    x = rng.integers(-2 ** 10, 2 ** 10 + 1, size=(4, K)).astype(np.float64)
+    s = synth.rademacher(K, rng)
+    back = O.fwht(O.rht(x, s, np.float64, 64), 64) * s.astype(np.float64) / 64.0
+    assert np.array_equal(back, x)
+    W = rng.standard_normal((64, K))
+    xf = rng.standard_normal((2, K))
+    y0 = xf @ W.T
+    y1 = O.rht(xf, s, np.float64, 64) @ O.rht(W, s, np.float64, 64).T / 64.0
+    assert np.max(np.abs(y1 - y0)) / np.max(np.abs(y0)) <= 1e-12
+
+
+def test_outlier_spreads_over_64_values():
+    # one value A becomes 64 values of magnitude A: max/rms of its block drops
+    # from sqrt(64) = 8 to 1 (from sqrt(32) with the pages' block)
+    K = 128
+    A = 1000.0
+    for j in (0, 33, 70, 127):
+        x = np.zeros(K, np.float32)
+        x[j] = A
+        u = O.rht(x, synth.rademacher(K, np.random.default_rng(j)), np.float32, 64)
+        b0 = (j // 64) * 64
+        assert np.all(np.abs(u[b0:b0 + 64]) == A)
+        assert np.all(np.delete(u, np.arange(b0, b0 + 64)) == 0)
+
+
+def test_activation_scale_carries_one_over_block():
+    # the same rotated row gives the same codes; the scale carries 1/B
+    u = np.array([[3.0, -127.0, 0.5, 64.0] * 16], dtype=np.float32)
+    q32, s32 = O.act_quant_i8(u, 32)
+    q64, s64 = O.act_quant_i8(u, 64)
+    assert np.array_equal(q32, q64)
+    assert s32[0] == np.float32(1.0 / 32) and s64[0] == np.float32(1.0 / 64)  # sigma = 127/127 = 1
+
+
+def test_block64_linear_matches_the_unrotated_product():
+    # the whole W4A8 layer with the 64-block transform approximates x . W^T
+    # as well as the 32-block one (4-bit quantization error only, ~10%; a
+    # wrong overall scale would be off by a factor of two)
+    x, W, signs = synth.random_case(2, 48, 256, seed=5)
+    y_ref = x.astype(np.float64) @ W.T.astype(np.float64)
+    err = {}
+    for block in (32, 64):
+        y, _S, _q, _s = O.linear_w4(x, signs, O.prepare_w4(W, signs, 64, block))
+        err[block] = np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
+        assert err[block] < 0.2
+    assert err[64] < 1.5 * err[32]
+
+
 @pytest.mark.parametrize("shape", [(1, 1024, 1024), (1, 4096, 512)])
 def test_rotated_product_preserved_fp64(shape):
     M, K, N = shape
