@@ -28,9 +28,13 @@
  *    the contract.
  *
  * The rotation is unnormalised (entries +/-1); the overall scale of the
- * transform on both operands, 1/sqrt(32) twice = 2^-5, is folded exactly into
- * x_scale.  One Hadamard ordering is used throughout: Sylvester natural order,
- * H[i][j] = (-1)^popcount(i & j).
+ * transform on both operands, 1/sqrt(B) twice = 1/B for a transform block of
+ * B values (2^-5 for the pages' B = 32), is folded exactly into x_scale.  One
+ * Hadamard ordering is used throughout: Sylvester natural order,
+ * H[i][j] = (-1)^popcount(i & j).  B = 64 is a variant sized to the 64-lane
+ * wave (the pages size the block to their 32-wide SIMD group): the butterfly
+ * has one more stage (h = 32).  Weights and the activations they meet must
+ * use the same B.
  */
 #ifndef SVGEMM_H
 #define SVGEMM_H
@@ -46,7 +50,7 @@ typedef int svg_status;
 enum {
     SVG_OK = 0,
     SVG_EINVAL = 1,        /* null required pointer, negative size, K <= 0      */
-    SVG_EUNSUPPORTED = 2,  /* block != 32, K % 32, K % group, group not in
+    SVG_EUNSUPPORTED = 2,  /* block not 32 or 64, K % 32, K % block, K % group, group not in
                               {32, 64, 128}, M > 32, unknown fmt, W8 K > 131072 */
     SVG_EALIGN = 3,        /* a pointer below its required alignment          */
     SVG_EHIP = 4           /* a HIP launch or runtime error (text in
@@ -100,7 +104,7 @@ svg_status svg_weight_sizes(int N, int K, int fmt, int group, uint64_t* wq_bytes
  *  signs    int8 [K], each +1 or -1; the same vector must be given to
  *           act_rht_quant_i8 for the activations this matrix consumes.
  *           4-byte aligned.
- *  block    transform block; must be 32.
+ *  block    transform block, 32 (the pages') or 64; K must be a multiple of it.
  *  fmt      SVG_W4_ASYM_Z4, SVG_W4_ASYM_Z16 or SVG_W8_SYM.
  *  group    W4: quantization group along K, 32, 64 or 128 (independent of the
  *           transform block).  Ignored for W8.
@@ -110,8 +114,8 @@ svg_status svg_weight_sizes(int N, int K, int fmt, int group, uint64_t* wq_bytes
  *           written as zeros.
  *  w_rot_debug  nullable fp32 [N][K]: receives the rotated rows u (tests).
  *
- *  Per row, u = H_32 . diag(signs) . W[n] blockwise (butterfly stages
- *  h = 1, 2, 4, 8, 16 in that order).  W4 per group: lo = min(0, min u),
+ *  Per row, u = H_B . diag(signs) . W[n] blockwise (butterfly stages
+ *  h = 1, 2, 4, ..., B/2 in that order).  W4 per group: lo = min(0, min u),
  *  hi = max(0, max u), s = fp16(rne((hi - lo) / 15)) (1.0 if zero),
  *  z = rint(-lo / s), q = clamp(rint(u / s) + z, 0, 15).  W8 per row:
  *  s = fp16(rne(max|u| / 127)) (1.0 if zero), q = clamp(rint(u / s), -127, 127).
@@ -132,16 +136,16 @@ svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
  *
  *  X        fp32 [M][K] row-major, 16-byte aligned.  M <= 32.
  *  signs    int8 [K] (+/-1), 4-byte aligned; the weights' sign vector.
- *  block    must be 32.
+ *  block    32 or 64, as for the weights this row meets; K % block == 0.
  *  xq       M*K int8 codes in [-127, 127], 16-byte aligned, in 32-k slabs:
  *           the code of (row m, k) is byte ((k / 32) * M + m) * 32 + k % 32,
  *           i.e. slab s = k / 32 holds the 32 codes of row 0, then row 1, ...
  *           (for M = 1 this is the row itself).  The linears read 16 rows of
  *           a 64-k run as two contiguous 512-byte pieces this way.
- *  x_scale  fp32 [M]: (max_k |u| / 127) * 2^-5 (0 for an all-zero row); 4-byte
- *           aligned.
+ *  x_scale  fp32 [M]: (max_k |u| / 127) / block (0 for an all-zero row);
+ *           4-byte aligned.
  *
- *  u = H_32 . diag(signs) . X[m] blockwise; sigma = max|u| / 127;
+ *  u = H_B . diag(signs) . X[m] blockwise; sigma = max|u| / 127;
  *  q = clamp(rint(u / sigma), -127, 127) (0 if the row is zero).
  */
 svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs,
@@ -203,9 +207,9 @@ svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
  *                    separate calls.
  *  wq ... partials_debug   as for w4a8_linear / w8a8_linear.
  *
- *  For M = 1 (M <= 2 with 32-wide groups) and K <= 12288 this is ONE launch:
- *  every workgroup quantizes the row itself while its first weights are in
- *  flight.  Otherwise it enqueues the two launches.  Errors as for the two separate calls; N == 0 runs the
+ *  For M = 1 (M <= 2 with 32-wide groups), K <= 12288 and block 32 this is
+ *  ONE launch: every workgroup quantizes the row itself while its first
+ *  weights are in flight.  Otherwise it enqueues the two launches.  Errors as for the two separate calls; N == 0 runs the
  *  quantization alone.
  */
 svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,

@@ -418,7 +418,7 @@ hipError_t dispatch_g(const LinArgs& a, const ActIn* f, hipStream_t stream) {
     // no MFMA form for 32-wide groups: the dot kernel, 8 tokens per launch,
     // after a separate quantization of all rows when the input is fp32
     if (f) {
-      hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, const_cast<int8_t*>(a.xq),
+      hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, f->block, const_cast<int8_t*>(a.xq),
                                               const_cast<float*>(a.x_scale), stream);
       if (e != hipSuccess) return e;
     }
@@ -444,10 +444,10 @@ hipError_t dispatch_g(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 
 hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
-                           float* y, int32_t* dbg, const float* X, const int8_t* signs,
+                           float* y, int32_t* dbg, const float* X, const int8_t* signs, int block,
                            hipStream_t stream) {
   const LinArgs a{xq, x_scale, M, K, wq, w_scale, w_zero, N, y, dbg, M, 0};
-  const ActIn fa{X, signs};
+  const ActIn fa{X, signs, block};
   const ActIn* f = X ? &fa : nullptr;
 #define SVG_G_CASE(G)                                                                                  \
   if (group == G) {                                                                                    \

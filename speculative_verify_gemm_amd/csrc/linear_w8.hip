@@ -217,9 +217,9 @@ struct MfmaW8 : W8Common {
 
 hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
-                           const int8_t* signs, hipStream_t stream) {
+                           const int8_t* signs, int block, hipStream_t stream) {
   const LinArgs a{xq, x_scale, M, K, wq, w_scale, nullptr, N, y, dbg, M, 0};
-  const ActIn fa{X, signs};
+  const ActIn fa{X, signs, block};
   const ActIn* f = X ? &fa : nullptr;
   if (M <= 1) return launch_linear_auto<DotW8<1>>(a, f, stream);
   if (M <= 16) return launch_linear_auto<MfmaW8<1>>(a, f, stream);

@@ -1,4 +1,6 @@
 // Block-diagonal random Hadamard transform fused with quantization, gfx950.
+// Every kernel takes the transform block B as a template argument: 32 (the
+// pages' block) or 64 (the wave-wide variant, one more butterfly stage).
 //
 //  * k_act_rht_quant   -- activations: sign flip + 32-wide butterfly, per-row
 //                         |u| max, int8 codes and the per-row scale (one
@@ -32,8 +34,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Load 4 values and their 4 signs, flip and transform.  `valid` is uniform
-// over each 8-lane block because K is a multiple of 32.
+// Load 4 values and their 4 signs, flip and transform (block B).  `valid` is
+// uniform over each B/4-lane block because K is a multiple of B.
+template <int B>
 SVG_DEV void rotate_chunk(const float* __restrict__ row, const int8_t* __restrict__ signs, int c,
                           bool valid, float& e0, float& e1, float& e2, float& e3) {
   if (valid) {
@@ -44,7 +47,7 @@ SVG_DEV void rotate_chunk(const float* __restrict__ row, const int8_t* __restric
   } else {
     e0 = e1 = e2 = e3 = 0.f;
   }
-  fwht32_lane4(e0, e1, e2, e3);
+  fwht_lane4<B>(e0, e1, e2, e3);
 }
 
 // Max over the workgroup (exact: max is order-free).
@@ -63,13 +66,14 @@ SVG_DEV float block_max(float v, float* red) {
 
 #pragma clang fp contract(off)
 
-template <int NT, int CPT>
+template <int NT, int CPT, int B>
 __global__ __launch_bounds__(NT) void k_act_rht_quant(const float* __restrict__ X, int K,
                                                      const int8_t* __restrict__ signs,
                                                      int8_t* __restrict__ xq, float* __restrict__ x_scale) {
   __shared__ float red[16];
   const int m = blockIdx.x;
-  act_quant_row<CPT>(X + (size_t)m * K, K, signs, StoreGlobal(xq, m, gridDim.x, x_scale + m, K), red);
+  act_quant_row<CPT, StoreGlobal, B>(X + (size_t)m * K, K, signs, StoreGlobal(xq, m, gridDim.x, x_scale + m, K),
+                                     red);
 }
 
 // Group-wise min/max over the LPG = G/4 lanes that hold one quantization group.
@@ -110,7 +114,7 @@ SVG_DEV size_t w4_param_index(int n, int g, int KB, int gpb) {
   return (((size_t)i * KB + jb) * 16 + r) * gpb + c;
 }
 
-template <int G, bool Z4>
+template <int G, bool Z4, int B>
 __global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restrict__ W, int K,
                                                           const int8_t* __restrict__ signs,
                                                           uint8_t* __restrict__ wq,
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restri
     const int c = c0 + threadIdx.x;
     const bool valid = c < nchunk;  // uniform over each group since K % G == 0
     float e0, e1, e2, e3;
-    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    rotate_chunk<B>(row, signs, c, valid, e0, e1, e2, e3);
     if (w_rot != nullptr && valid)
       *reinterpret_cast<float4*>(w_rot + (size_t)n * K + 4 * c) = make_float4(e0, e1, e2, e3);
     const float mn = group_min<LPG>(fminf(fminf(e0, e1), fminf(e2, e3)));
@@ -180,6 +184,7 @@ SVG_DEV size_t w8_offset(int n, int k, int KT8) {
   return ((size_t)i * KT8 + j) * 1024 + (size_t)(16 * (kc >> 4) + r) * 16 + (kc & 15);
 }
 
+template <int B>
 __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restrict__ W, int K,
                                                           const int8_t* __restrict__ signs,
                                                           int8_t* __restrict__ wq,
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restri
     const int c = c0 + threadIdx.x;
     const bool valid = c < nchunk;
     float e0, e1, e2, e3;
-    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    rotate_chunk<B>(row, signs, c, valid, e0, e1, e2, e3);
     if (valid) {
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0), fabsf(e1)), fmaxf(fabsf(e2), fabsf(e3))));
       if (w_rot != nullptr)
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w8(const float* __restri
     const int c = c0 + threadIdx.x;
     const bool valid = c < nchunk;
     float e0, e1, e2, e3;
-    rotate_chunk(row, signs, c, valid, e0, e1, e2, e3);
+    rotate_chunk<B>(row, signs, c, valid, e0, e1, e2, e3);
     if (valid) {
       const int q0 = clamp_i((int)rintf(e0 / s), -127, 127);
       const int q1 = clamp_i((int)rintf(e1 / s), -127, 127);
@@ -232,12 +237,13 @@ __global__ __launch_bounds__(kThreads) void k_fill_zero(u32* __restrict__ p, siz
 
 }  // namespace
 
-hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int8_t* xq,
-                                    float* x_scale, hipStream_t stream) {
+template <int B>
+static void launch_act(const float* X, int M, int K, const int8_t* signs, int8_t* xq, float* x_scale,
+                       hipStream_t stream) {
   const int nchunk = K / 4;  // float4 chunks of a row
   const dim3 grid(M);
 #define SVG_ACT(NT, CPT) \
-  hipLaunchKernelGGL((k_act_rht_quant<NT, CPT>), grid, dim3(NT), 0, stream, X, K, signs, xq, x_scale)
+  hipLaunchKernelGGL((k_act_rht_quant<NT, CPT, B>), grid, dim3(NT), 0, stream, X, K, signs, xq, x_scale)
   if (nchunk <= 256) SVG_ACT(256, 1);
   else if (nchunk <= 512) SVG_ACT(512, 1);
   else if (nchunk <= 1024) SVG_ACT(1024, 1);
@@ -247,6 +253,12 @@ hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* 
   else if (nchunk <= 6144) SVG_ACT(1024, 6);
   else SVG_ACT(1024, 8);  // past 8192 chunks the row is read twice
 #undef SVG_ACT
+}
+
+hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int block, int8_t* xq,
+                                    float* x_scale, hipStream_t stream) {
+  if (block == 64) launch_act<64>(X, M, K, signs, xq, x_scale, stream);
+  else launch_act<32>(X, M, K, signs, xq, x_scale, stream);
   return hipGetLastError();
 }
 
@@ -258,7 +270,7 @@ static hipError_t fill_zero(void* p, size_t nbytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* signs, int group,
+hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* signs, int block, int group,
                                    bool z4, uint8_t* wq, uint16_t* w_scale, void* w_zero,
                                    float* w_rot, hipStream_t stream) {
   if (N % 16 || K % kMetaK) {  // the tiled/blocked storage has padding: clear it first
@@ -269,25 +281,28 @@ hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* s
     if ((e = fill_zero(w_scale, sb, stream)) != hipSuccess) return e;
     if ((e = fill_zero(w_zero, zb, stream)) != hipSuccess) return e;
   }
-  const dim3 grid(N), block(kThreads);
-#define SVG_W4_CASE(G)                                                                            \
-  if (group == G) {                                                                               \
+  const dim3 grid(N), threads(kThreads);
+#define SVG_W4_CASE(G, B)                                                                         \
+  if (group == G && block == B) {                                                                 \
     if (z4)                                                                                       \
-      hipLaunchKernelGGL((k_rot_quant_w4<G, true>), grid, block, 0, stream, W, K, signs, wq,      \
+      hipLaunchKernelGGL((k_rot_quant_w4<G, true, B>), grid, threads, 0, stream, W, K, signs, wq, \
                          w_scale, w_zero, w_rot);                                                 \
     else                                                                                          \
-      hipLaunchKernelGGL((k_rot_quant_w4<G, false>), grid, block, 0, stream, W, K, signs, wq,     \
-                         w_scale, w_zero, w_rot);                                                 \
+      hipLaunchKernelGGL((k_rot_quant_w4<G, false, B>), grid, threads, 0, stream, W, K, signs,    \
+                         wq, w_scale, w_zero, w_rot);                                             \
     return hipGetLastError();                                                                     \
   }
-  SVG_W4_CASE(32)
-  SVG_W4_CASE(64)
-  SVG_W4_CASE(128)
+  SVG_W4_CASE(32, 32)
+  SVG_W4_CASE(64, 32)
+  SVG_W4_CASE(128, 32)
+  SVG_W4_CASE(32, 64)
+  SVG_W4_CASE(64, 64)
+  SVG_W4_CASE(128, 64)
 #undef SVG_W4_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* signs, int8_t* wq,
+hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* signs, int block, int8_t* wq,
                                    uint16_t* w_scale, float* w_rot, hipStream_t stream) {
   if (N % 16 || K % 64) {
     size_t wb, sb;
@@ -295,7 +310,9 @@ hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* s
     hipError_t e = fill_zero(wq, wb, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_rot_quant_w8, dim3(N), dim3(kThreads), 0, stream, W, K, signs, wq, w_scale,
-                     w_rot);
+  if (block == 64)
+    hipLaunchKernelGGL(k_rot_quant_w8<64>, dim3(N), dim3(kThreads), 0, stream, W, K, signs, wq, w_scale, w_rot);
+  else
+    hipLaunchKernelGGL(k_rot_quant_w8<32>, dim3(N), dim3(kThreads), 0, stream, W, K, signs, wq, w_scale, w_rot);
   return hipGetLastError();
 }

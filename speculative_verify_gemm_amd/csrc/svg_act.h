@@ -8,10 +8,12 @@
 // pass": random sign flips, then a +/-1 Hadamard on each block of 32 values,
 // then 8-bit quantization on the fly.  Per token: amax = max |u|,
 // sigma = amax / 127, q = clamp(rint(u / sigma), -127, 127), stored scale
-// sigma * 2^-5 (the transform's overall scale on both operands).
+// sigma / B (the transform's overall scale on both operands; 2^-5 for the
+// pages' block B = 32, 2^-6 for the wave-wide block 64).
 //
 // Thread i holds float4 chunks i, i + NT, i + 2 NT, ... (NT threads), so a
-// 32-block spans 8 consecutive lanes and the butterfly is lane exchanges only.
+// 32-block spans 8 consecutive lanes (a 64-block 16) and the butterfly is
+// lane exchanges only.
 //
 // The code of every value is the one IEEE division u / sigma (correctly
 // rounded) followed by round-half-to-even gives.  Dividing is slow, so the
@@ -52,14 +54,15 @@ SVG_DEV float wg_max(float v, float* red) {
 }
 
 // Rotated values of float4 chunk c of a row: loads (zeros past the row),
-// sign flip, 32-wide butterfly.
+// sign flip, B-wide butterfly.
+template <int B>
 SVG_DEV void act_rotate4(rsrc_t xr, rsrc_t sr, u32 c, float e[4]) {
   const u32x4 v = bload16(xr, c * 16u);
   const int sg = (int)bload4(sr, c * 4u);
   e[0] = __uint_as_float(v[0]); e[1] = __uint_as_float(v[1]);
   e[2] = __uint_as_float(v[2]); e[3] = __uint_as_float(v[3]);
   apply_signs4(e[0], e[1], e[2], e[3], sg);
-  fwht32_lane4(e[0], e[1], e[2], e[3]);
+  fwht_lane4<B>(e[0], e[1], e[2], e[3]);
 }
 
 SVG_DEV u32 pack4(const int q[4]) {
@@ -114,29 +117,30 @@ SVG_DEV void act_load_row(const float* x, int K, const int8_t* signs, RowRegs<CP
   }
 }
 
-// Sign flip and butterfly of a row loaded by act_load_row; returns this
-// thread's max |u|.
-template <int CPT>
+// Sign flip and butterfly (block B) of a row loaded by act_load_row; returns
+// this thread's max |u|.
+template <int CPT, int B = 32>
 SVG_DEV float act_rotate_loaded(RowRegs<CPT>& r) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     apply_signs4(r.e[i][0], r.e[i][1], r.e[i][2], r.e[i][3], r.sg[i]);
-    fwht32_lane4(r.e[i][0], r.e[i][1], r.e[i][2], r.e[i][3]);
+    fwht_lane4<B>(r.e[i][0], r.e[i][1], r.e[i][2], r.e[i][3]);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(r.e[i][0]), fabsf(r.e[i][1])), fmaxf(fabsf(r.e[i][2]), fabsf(r.e[i][3]))));
   }
   return amax;
 }
 
-// Codes and scale of a rotated row whose max |u| over the row is amax.
-template <int CPT, class Store>
+// Codes and scale of a rotated row whose max |u| over the row is amax (B:
+// the transform block, whose overall scale 1/B the stored scale carries).
+template <int CPT, class Store, int B = 32>
 SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Store& st,
                              u32 tid = threadIdx.x, u32 NT = blockDim.x) {
   const u32 nchunk = (u32)K >> 2;
   const float sigma = amax / 127.0f;
   const float rinv = 1.0f / sigma;
   const bool fast = sigma >= 0x1p-125f;
-  if (tid == 0) st.scale(sigma * 0.03125f);  // exact: carries the transform's 2^-5
+  if (tid == 0) st.scale(sigma * (1.0f / B));  // exact: a power of two
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const u32 c = tid + NT * i;
@@ -153,10 +157,10 @@ SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Sto
 
 // Rotate and quantize a row loaded by act_load_row (K <= 4 * NT * CPT); codes
 // and the scale go to `st`.  Every thread of the workgroup must call it.
-template <int CPT, class Store>
+template <int CPT, class Store, int B = 32>
 SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* red) {
-  const float amax = wg_max(act_rotate_loaded<CPT>(r), red);
-  act_store_codes<CPT>(r, K, amax, st);
+  const float amax = wg_max(act_rotate_loaded<CPT, B>(r), red);
+  act_store_codes<CPT, Store, B>(r, K, amax, st);
 }
 
 // Maxima of R values over the workgroup with one LDS round.  red: >= 16 * R.
@@ -199,17 +203,17 @@ SVG_DEV void act_quant_rows_lds(const float* X, int M, int K, const int8_t* sign
     if (r < M) act_store_codes<CPT>(rr[r], K, amax[r], StoreLds{out + r * stride, scale + r});
 }
 
-// Rotate and quantize row `x` (K values, K % 32 == 0); codes and the scale
-// go to `st`.  Every thread of the workgroup must call it.  The row is held
-// in registers when K <= 4 * NT * CPT (one read of the input); longer rows
-// are read twice (the second pass recomputes the same rotated values).
-template <int CPT, class Store>
+// Rotate (block B) and quantize row `x` (K values, K % B == 0); codes and the
+// scale go to `st`.  Every thread of the workgroup must call it.  The row is
+// held in registers when K <= 4 * NT * CPT (one read of the input); longer
+// rows are read twice (the second pass recomputes the same rotated values).
+template <int CPT, class Store, int B = 32>
 SVG_DEV void act_quant_row(const float* x, int K, const int8_t* signs, const Store& st, float* red) {
   const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
   if (nchunk <= NT * CPT) {
     RowRegs<CPT> r;
     act_load_row<CPT>(x, K, signs, r);
-    act_quant_loaded<CPT>(r, K, st, red);
+    act_quant_loaded<CPT, Store, B>(r, K, st, red);
     return;
   }
   const rsrc_t xr = make_rsrc(x, (u32)K * 4u);
@@ -217,17 +221,17 @@ SVG_DEV void act_quant_row(const float* x, int K, const int8_t* signs, const Sto
   float amax = 0.f;
   for (u32 c = threadIdx.x; c < nchunk; c += NT) {
     float e[4];
-    act_rotate4(xr, sr, c, e);
+    act_rotate4<B>(xr, sr, c, e);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))));
   }
   amax = wg_max(amax, red);
   const float sigma = amax / 127.0f;
   const float rinv = 1.0f / sigma;
   const bool fast = sigma >= 0x1p-125f;
-  if (threadIdx.x == 0) st.scale(sigma * 0.03125f);
+  if (threadIdx.x == 0) st.scale(sigma * (1.0f / B));
   for (u32 c = threadIdx.x; c < nchunk; c += NT) {
     float e[4];
-    act_rotate4(xr, sr, c, e);
+    act_rotate4<B>(xr, sr, c, e);
     int q[4] = {0, 0, 0, 0};
     if (amax > 0.f) {
 #pragma unroll

@@ -68,6 +68,22 @@ SVG_DEV void fwht32_lane4(float& e0, float& e1, float& e2, float& e3) {
   }
 }
 
+// Transform block B = 32 or 64 (the wave-wide variant).  A 64-block spans 16
+// consecutive lanes: the 32-wide butterfly runs on each half (lanes j and
+// j ^ 8 hold elements i and i + 32), then the stage h = 32 pairs them, the
+// lower element becoming (a + b) and the upper one (a - b) as at every stage.
+template <int B>
+SVG_DEV void fwht_lane4(float& e0, float& e1, float& e2, float& e3) {
+  static_assert(B == 32 || B == 64, "transform block 32 or 64");
+  fwht32_lane4(e0, e1, e2, e3);
+  if constexpr (B == 64) {
+    const float p0 = lane_xorf<8>(e0), p1 = lane_xorf<8>(e1), p2 = lane_xorf<8>(e2), p3 = lane_xorf<8>(e3);
+    const bool up = __lane_id() & 8;                               // h = 32
+    e0 = up ? p0 - e0 : e0 + p0; e1 = up ? p1 - e1 : e1 + p1;
+    e2 = up ? p2 - e2 : e2 + p2; e3 = up ? p3 - e3 : e3 + p3;
+  }
+}
+
 // Sign flip of four values by four packed int8 signs (+1 / -1): exact.
 SVG_DEV void apply_signs4(float& e0, float& e1, float& e2, float& e3, int packed) {
   e0 = e0 * (float)(int8_t)(packed & 0xFF);

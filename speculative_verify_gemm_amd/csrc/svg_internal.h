@@ -5,24 +5,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int8_t* xq,
+// `block`: the transform block, 32 or 64 (checked by the caller).
+hipError_t svg_launch_act_rht_quant(const float* X, int M, int K, const int8_t* signs, int block, int8_t* xq,
                                     float* x_scale, hipStream_t stream);
-hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* signs, int group,
+hipError_t svg_launch_rot_quant_w4(const float* W, int N, int K, const int8_t* signs, int block, int group,
                                    bool z4, uint8_t* wq, uint16_t* w_scale, void* w_zero,
                                    float* w_rot, hipStream_t stream);
-hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* signs, int8_t* wq,
+hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* signs, int block, int8_t* wq,
                                    uint16_t* w_scale, float* w_rot, hipStream_t stream);
 // The linears read int8 codes xq / x_scale; with X != nullptr they first
-// produce them from the fp32 rows X (and signs), writing xq / x_scale as
-// outputs (inside the linear's own launch for M <= 2, in a launch of their
-// own before it otherwise).
+// produce them from the fp32 rows X (signs, transform block), writing xq /
+// x_scale as outputs (inside the linear's own launch for M = 1 with the
+// 32-block, in a launch of their own before it otherwise).
 hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
-                           float* y, int32_t* dbg, const float* X, const int8_t* signs,
+                           float* y, int32_t* dbg, const float* X, const int8_t* signs, int block,
                            hipStream_t stream);
 hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
-                           const int8_t* signs, hipStream_t stream);
+                           const int8_t* signs, int block, hipStream_t stream);
 
 // Greedy acceptance of a draft tree (tree_accept.hip); `workspace` is the
 // caller's zero-filled SVG_TREE_WORKSPACE_BYTES, left zero-filled.

@@ -190,6 +190,7 @@ constexpr int fused_rows() { return P::kMaxTok <= 2 ? P::kMaxTok : 0; }
 struct ActIn {
   const float* X;
   const int8_t* signs;
+  int block;  // transform block; the fused kernel takes the pages' 32 only
 };
 
 template <class P, int WAVES, int CPW, int U>
@@ -305,8 +306,8 @@ hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 template <class P>
 hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
-  if (f && (a.M > fused_rows<P>() || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
-    hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, const_cast<int8_t*>(a.xq),
+  if (f && (a.M > fused_rows<P>() || a.K > kLdsMaxK || f->block != 32)) {  // not fusable: quantize in a launch of their own
+    hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, f->block, const_cast<int8_t*>(a.xq),
                                             const_cast<float*>(a.x_scale), stream);
     if (e != hipSuccess) return e;
     f = nullptr;

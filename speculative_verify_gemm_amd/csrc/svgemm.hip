@@ -35,6 +35,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
 
+// Transform blocks: the pages' 32, and 64 (one wave of 64 lanes, 16 of them
+// per block).
+bool block_ok(int b) { return b == 32 || b == 64; }
+
 constexpr int kMaxM = 32;
 constexpr int kMaxKW8 = 131072;  // 127^2 * K < 2^31
 
@@ -86,8 +90,9 @@ svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
   if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
   if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16 && fmt != SVG_W8_SYM)
     return fail(SVG_EUNSUPPORTED, fn, "unknown fmt");
-  if (block != 32) return fail(SVG_EUNSUPPORTED, fn, "block must be 32");
+  if (!block_ok(block)) return fail(SVG_EUNSUPPORTED, fn, "block must be 32 or 64");
   if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  if (K % block) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of block");
   const bool w4 = fmt != SVG_W8_SYM;
   if (w4 && !group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
   if (w4 && K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of group");
@@ -102,10 +107,10 @@ svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (w4)
-    e = svg_launch_rot_quant_w4(W, N, K, signs, group, fmt == SVG_W4_ASYM_Z4,
+    e = svg_launch_rot_quant_w4(W, N, K, signs, block, group, fmt == SVG_W4_ASYM_Z4,
                                 reinterpret_cast<uint8_t*>(wq), w_scale, w_zero, w_rot_debug, s);
   else
-    e = svg_launch_rot_quant_w8(W, N, K, signs, reinterpret_cast<int8_t*>(wq), w_scale, w_rot_debug, s);
+    e = svg_launch_rot_quant_w8(W, N, K, signs, block, reinterpret_cast<int8_t*>(wq), w_scale, w_rot_debug, s);
   return hip_status(fn, e);
 }
 
@@ -114,14 +119,15 @@ svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs, i
   static const char* fn = "act_rht_quant_i8";
   if (M < 0) return fail(SVG_EINVAL, fn, "M < 0");
   if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
-  if (block != 32) return fail(SVG_EUNSUPPORTED, fn, "block must be 32");
+  if (!block_ok(block)) return fail(SVG_EUNSUPPORTED, fn, "block must be 32 or 64");
   if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  if (K % block) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of block");
   if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
   if (!X || !signs || !xq || !x_scale) return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(X, 16) || !aligned(xq, 16)) return fail(SVG_EALIGN, fn, "X and xq need 16-byte alignment");
   if (!aligned(signs, 4) || !aligned(x_scale, 4)) return fail(SVG_EALIGN, fn, "signs / x_scale need 4-byte alignment");
   if (M == 0) return ok();
-  return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, xq, x_scale,
+  return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, block, xq, x_scale,
                                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -162,9 +168,10 @@ svg_status check_w8(const char* fn, const int8_t* xq, const float* x_scale, int 
 }
 
 // The fp32 input of the fused calls: X, signs and block.
-svg_status check_fused_input(const char* fn, const float* X, const int8_t* signs, int block) {
+svg_status check_fused_input(const char* fn, const float* X, const int8_t* signs, int block, int K) {
   if (!X || !signs) return fail(SVG_EINVAL, fn, "null required pointer");
-  if (block != 32) return fail(SVG_EUNSUPPORTED, fn, "block must be 32");
+  if (!block_ok(block)) return fail(SVG_EUNSUPPORTED, fn, "block must be 32 or 64");
+  if (K % block) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of block");
   if (!aligned(X, 16)) return fail(SVG_EALIGN, fn, "X needs 16-byte alignment");
   if (!aligned(signs, 4)) return fail(SVG_EALIGN, fn, "signs needs 4-byte alignment");
   return SVG_OK;
@@ -182,7 +189,7 @@ svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (st != SVG_OK) return st;
   if (M == 0 || N == 0) return ok();
   return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
-                                        group, N, y, partials_debug, nullptr, nullptr,
+                                        group, N, y, partials_debug, nullptr, nullptr, 32,
                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -194,7 +201,7 @@ svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (st != SVG_OK) return st;
   if (M == 0 || N == 0) return ok();
   return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, nullptr,
-                                        nullptr, reinterpret_cast<hipStream_t>(stream)));
+                                        nullptr, 32, reinterpret_cast<hipStream_t>(stream)));
 }
 
 svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
@@ -203,13 +210,13 @@ svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* sig
                                  int32_t* partials_debug, void* stream) {
   static const char* fn = "act_quant_w4a8_linear";
   svg_status st = check_w4(fn, xq, x_scale, M, K, wq, w_scale, w_zero, fmt, group, N, y, partials_debug);
-  if (st == SVG_OK) st = check_fused_input(fn, X, signs, block);
+  if (st == SVG_OK) st = check_fused_input(fn, X, signs, block, K);
   if (st != SVG_OK) return st;
   if (M == 0) return ok();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, xq, x_scale, s));
+  if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, block, xq, x_scale, s));
   return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
-                                        group, N, y, partials_debug, X, signs, s));
+                                        group, N, y, partials_debug, X, signs, block, s));
 }
 
 svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
@@ -217,12 +224,12 @@ svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* sig
                                  int N, float* y, int32_t* partials_debug, void* stream) {
   static const char* fn = "act_quant_w8a8_linear";
   svg_status st = check_w8(fn, xq, x_scale, M, K, wq, w_scale, N, y, partials_debug);
-  if (st == SVG_OK) st = check_fused_input(fn, X, signs, block);
+  if (st == SVG_OK) st = check_fused_input(fn, X, signs, block, K);
   if (st != SVG_OK) return st;
   if (M == 0) return ok();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, xq, x_scale, s));
-  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, X, signs, s));
+  if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, block, xq, x_scale, s));
+  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, X, signs, block, s));
 }
 
 svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,

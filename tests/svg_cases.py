@@ -23,15 +23,15 @@ def to_dev(a, dtype=None):
     return t.to(DEV)
 
 
-def gpu_quant_acts(x, signs):
+def gpu_quant_acts(x, signs, block=32):
     M, K = x.shape
     xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
     xs = torch.empty((M,), dtype=torch.float32, device=DEV)
-    svg.act_rht_quant_i8(to_dev(x), to_dev(signs), xq, xs)
+    svg.act_rht_quant_i8(to_dev(x), to_dev(signs), xq, xs, block=block)
     return xq, xs
 
 
-def gpu_prepare(W, signs, fmt, group, debug=False, poison=True):
+def gpu_prepare(W, signs, fmt, group, debug=False, poison=True, block=32):
     """W: numpy [N,K] fp32 or a device tensor.  The storage is first filled
     with a non-zero byte so that padding the library fails to write shows."""
     Wd = W if isinstance(W, torch.Tensor) else to_dev(W)
@@ -42,8 +42,8 @@ def gpu_prepare(W, signs, fmt, group, debug=False, poison=True):
             if t is not None:
                 t.view(torch.uint8).fill_(0x5A)
     rot = torch.empty((N, K), dtype=torch.float32, device=DEV) if debug else None
-    svg.rht_rotate_weights(Wd, to_dev(signs), fmt, group, wq, ws, wz, rot)
-    return dict(wq=wq, ws=ws, wz=wz, rot=rot, fmt=fmt, group=group, N=N, K=K)
+    svg.rht_rotate_weights(Wd, to_dev(signs), fmt, group, wq, ws, wz, rot, block=block)
+    return dict(wq=wq, ws=ws, wz=wz, rot=rot, fmt=fmt, group=group, N=N, K=K, block=block)
 
 
 def gpu_linear(xq, xs, w, debug=True):
@@ -96,12 +96,14 @@ def gpu_fused(x, signs, w, debug=True):
     xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
     xs = torch.empty((M,), dtype=torch.float32, device=DEV)
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    block = w.get("block", 32)
     if w["fmt"] == "w8":
         dbg = torch.empty((M, N), dtype=torch.int32, device=DEV) if debug else None
-        svg.act_quant_w8a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], N, y, dbg)
+        svg.act_quant_w8a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], N, y, dbg, block=block)
     else:
         dbg = torch.empty((M, N, K // w["group"]), dtype=torch.int32, device=DEV) if debug else None
-        svg.act_quant_w4a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], w["wz"], w["fmt"], w["group"], N, y, dbg)
+        svg.act_quant_w4a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], w["wz"], w["fmt"], w["group"], N, y, dbg,
+                                  block=block)
     return xq, xs, y, dbg
 
 

@@ -64,6 +64,17 @@ def test_w4a8_validation(svg, kw, code):
     assert svg.last_error().startswith("w4a8_linear:")
 
 
+def test_transform_block_64_is_accepted_and_checked(svg):
+    # block 64 (K a multiple of 64) passes validation: empty calls return OK
+    assert svg.lib.act_rht_quant_i8(A, 0, 128, A, 64, A, A, NULL) == 0
+    assert svg.lib.rht_rotate_weights(A, 0, 128, A, 64, 1, 32, A, A, A, NULL, NULL) == 0
+    # K not a multiple of the block, and blocks other than 32 / 64
+    assert svg.lib.act_rht_quant_i8(A, 1, 96, A, 64, A, A, NULL) == 2
+    assert svg.lib.rht_rotate_weights(A, 4, 96, A, 64, 1, 32, A, A, A, NULL, NULL) == 2
+    assert svg.lib.rht_rotate_weights(A, 4, 128, A, 128, 1, 32, A, A, A, NULL, NULL) == 2
+    assert svg.lib.act_quant_w8a8_linear(A, 1, 96, A, 64, A, A, A, A, 16, A, NULL, NULL) == 2
+
+
 def test_empty_calls_are_ok(svg):
     assert _w4(svg, M=0) == 0 and svg.last_error() == ""
     assert _w4(svg, N=0) == 0
@@ -86,7 +97,7 @@ def test_act_quant_validation(svg, args, code):
     ((NULL, 4, 64, A, 32, 1, 32, A, A, A, NULL), 1),
     ((A, 4, 64, A, 32, 0, 32, A, A, NULL, NULL), 1),     # W4 needs w_zero
     ((A, 4, 64, A, 32, 3, 32, A, A, A, NULL), 2),        # unknown fmt
-    ((A, 4, 64, A, 64, 1, 32, A, A, A, NULL), 2),        # block != 32
+    ((A, 4, 64, A, 16, 1, 32, A, A, A, NULL), 2),        # block not 32 or 64
     ((A, 4, 96, A, 32, 1, 64, A, A, A, NULL), 2),        # K % group
     ((A, 4, 64, A, 32, 1, 48, A, A, A, NULL), 2),        # group
     ((A, 4, 64, MIS, 32, 1, 32, A, A, A, NULL), 3),      # signs alignment
@@ -118,7 +129,7 @@ def _fused4(svg, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(X=NULL), 1), (dict(signs=NULL), 1), (dict(xq=NULL), 1), (dict(wz=NULL), 1),
-    (dict(block=64), 2), (dict(M=33), 2), (dict(g=96), 2), (dict(fmt=2), 2),
+    (dict(block=16), 2), (dict(block=64, K=96), 2), (dict(M=33), 2), (dict(g=96), 2), (dict(fmt=2), 2),
     (dict(X=MIS), 3), (dict(xq=MIS), 3), (dict(signs=MIS), 3), (dict(wq=MIS), 3),
 ])
 def test_fused_w4_validation(svg, kw, code):

@@ -352,3 +352,62 @@ def test_stack_launch_sampled_rows(workload, M, launch):
     yh = C.host(y)
     check_y(yh[:, rows], y_ref)
     assert np.array_equal(C.host(y2).view(np.uint32), yh.view(np.uint32))
+
+
+# ------------------------------------------- the wave-wide transform block
+# Block 64 (a variant sized to the 64-lane wave): the same checks as for the
+# pages' 32, against the oracle run with block 64.
+ACT64_CASES = [(1, 64), (3, 192), (16, 4096), (5, 12288), (2, 40960)]
+
+
+@pytest.mark.parametrize("M,K", ACT64_CASES)
+def test_act_codes_block64(M, K):
+    C.say(f"act_rht_quant_i8 block=64 M={M} K={K}")
+    x, _W, signs = synth.random_case(M, 1, K, seed=M * 31 + K, x_kind="student_t3")
+    qx, sx = O.quant_acts(x, signs, 64)
+    xq, xs = C.gpu_quant_acts(x, signs, block=64)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+
+
+W64_CASES = [("w4_z4", 32, 64, 1024), ("w4_z16", 64, 48, 4096), ("w4_z16", 128, 37, 384),
+             ("w4_z4", 64, 33, 192), ("w8", 0, 45, 1152), ("w8", 0, 16, 64)]
+
+
+@pytest.mark.parametrize("fmt,group,N,K", W64_CASES)
+def test_weight_codes_block64(fmt, group, N, K):
+    C.say(f"rht_rotate_weights block=64 fmt={fmt} g={group} N={N} K={K}")
+    _x, W, signs = synth.random_case(1, N, K, seed=N + K + group + 64)
+    w = C.gpu_prepare(W, signs, fmt, group, debug=True, block=64)
+    u = O.rht(W, signs, np.float32, 64)
+    assert np.array_equal(C.host(w["rot"]).view(np.uint32), u.view(np.uint32))
+    if fmt == "w8":
+        q, s = O.quant_w8(u)
+        ow = dict(q=q, s=s)
+    else:
+        q, s, z = O.quant_w4(u, group)
+        ow = dict(q=q, s=s, z=z, group=group)
+    wq, ws, wz = C.oracle_storage(ow, fmt, K)
+    assert np.array_equal(C.host(w["wq"]).view(np.uint8), wq.view(np.uint8).reshape(-1))
+    assert np.array_equal(C.host(w["ws"]).view(np.uint16), ws.view(np.uint16).reshape(-1))
+    if wz is not None:
+        assert np.array_equal(C.host(w["wz"]).view(np.uint8), wz.view(np.uint8).reshape(-1))
+
+
+@pytest.mark.parametrize("fmt,group,M,N,K", [("w4_z16", 64, 1, 300, 4096), ("w4_z4", 32, 2, 64, 1024),
+                                             ("w4_z16", 128, 16, 130, 12288), ("w8", 0, 1, 70, 4096),
+                                             ("w8", 0, 32, 40, 12288)])
+def test_linear_block64_end_to_end(fmt, group, M, N, K):
+    """Weights and activations both rotated with 64-blocks, through the
+    fp32-input entry points (two launches for this block): codes, partial
+    sums and outputs against the oracle."""
+    C.say(f"block=64 linear fmt={fmt} g={group} M={M} N={N} K={K}")
+    x, W, signs = synth.random_case(M, N, K, seed=3 * M + N + K)
+    w = C.gpu_prepare(W, signs, fmt, group, block=64)
+    ow = O.prepare_w8(W, signs, 64) if fmt == "w8" else O.prepare_w4(W, signs, group, 64)
+    y_ref, S, qx, sx = (O.linear_w8 if fmt == "w8" else O.linear_w4)(x, signs, ow)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+    assert np.array_equal(C.host(dbg).astype(np.int64), S)
+    check_y(C.host(y), y_ref)
