@@ -79,12 +79,13 @@ def weight_bytes(N, K, fmt, group):
 class Stack:
     """The synthetic stack resident on the device, and its captured passes."""
 
-    def __init__(self, workload, layers, dev, fused=True):
+    def __init__(self, workload, layers, dev, fused=True, block=32):
         import torch
         import speculative_verify_gemm_amd as svg
         import synth
         self.torch, self.svg, self.synth = torch, svg, synth
         self.fused = fused
+        self.block = block
         self.wl = workload
         self.spec = WORKLOADS[workload]
         self.fmt, self.group = self.spec["fmt"], self.spec["group"]
@@ -103,7 +104,7 @@ class Stack:
                     W = synth.stack_weight(L, mname, device=dev)
                     n = W.shape[0]
                     mq, ms, mz = svg.stacked_slices(wq, ws, wz, r0, n, K, self.fmt, self.group)
-                    svg.rht_rotate_weights(W, signs[space], self.fmt, self.group, mq, ms, mz)
+                    svg.rht_rotate_weights(W, signs[space], self.fmt, self.group, mq, ms, mz, block=block)
                     r0 += n
                     del W
                 lw[name] = (wq, ws, wz, N)
@@ -135,9 +136,10 @@ class Stack:
             X, sg = io["xin"][L][space], self.signs[L][space]
             xq, xs, y = io["xq"][space], io["xs"][space], io["ys"][L][name]
             if self.fmt == "w8":
-                self.svg.act_quant_w8a8_linear(X, sg, xq, xs, wq, ws, N, y)
+                self.svg.act_quant_w8a8_linear(X, sg, xq, xs, wq, ws, N, y, block=self.block)
             else:
-                self.svg.act_quant_w4a8_linear(X, sg, xq, xs, wq, ws, wz, self.fmt, self.group, N, y)
+                self.svg.act_quant_w4a8_linear(X, sg, xq, xs, wq, ws, wz, self.fmt, self.group, N, y,
+                                               block=self.block)
             return
         if self.fmt == "w8":
             self.svg.w8a8_linear(io["xq"][space], io["xs"][space], wq, ws, N, io["ys"][L][name])
@@ -149,7 +151,7 @@ class Stack:
         """The separate activation step of the unfused pass (nothing when fused)."""
         if force or not self.fused:
             self.svg.act_rht_quant_i8(io["xin"][L][space], self.signs[L][space], io["xq"][space],
-                                      io["xs"][space])
+                                      io["xs"][space], block=self.block)
 
     def run_pass(self, io, events=None):
         for L in range(self.layers):
@@ -298,7 +300,8 @@ def cpu_baseline(stack, M, min_seconds=12.0, max_reps=32):
         Ws = [synth.stack_weight(0, m, device=stack.dev).cpu().numpy() for m in members]
         W = np.concatenate(Ws, axis=0)
         signs = synth.stack_signs(0, space)
-        ow = O.prepare_w8(W, signs) if stack.fmt == "w8" else O.prepare_w4(W, signs, stack.group)
+        ow = (O.prepare_w8(W, signs, stack.block) if stack.fmt == "w8"
+              else O.prepare_w4(W, signs, stack.group, stack.block))
         prepared.append((space, signs, ow, N, K))
         del W, Ws
     layer_bytes = sum(linear_bytes(M, N, K, stack.fmt, stack.group) for _sp, _s, _o, N, K in prepared)
@@ -383,6 +386,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the M=1 comparison pass")
     ap.add_argument("--sweep", default=None, help="comma-separated M values: report a pass per M")
+    ap.add_argument("--block", type=int, default=32, choices=(32, 64),
+                    help="transform block: the pages' 32, or the wave-wide 64")
     ap.add_argument("--tree-vocab", type=int, default=131072,
                     help="logits per node of the draft-tree acceptance measured after the pass (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -409,7 +414,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize(dev)
         del src, dst
-    stack = Stack(args.workload, args.layers, dev, fused=not args.unfused)
+    stack = Stack(args.workload, args.layers, dev, fused=not args.unfused, block=args.block)
     print(f"[bench] weights resident after {stack.setup_s:.1f} s", file=sys.stderr, flush=True)
 
     def measure(m):
@@ -450,6 +455,7 @@ def main():
         "kernel_digest": source_digest(),
         "config": {"workload": args.workload, "description": spec["desc"], "M": M,
                    "layers": args.layers, "weight_format": stack.fmt, "group": stack.group,
+                   "transform_block": args.block,
                    "bytes_per_pass": nbytes, "weight_bytes_per_pass": wbytes,
                    "launches_per_pass": args.layers * len(LAYER_LAUNCHES) * (1 if one else 2),
                    "fused_activation_quantization": one},

@@ -207,9 +207,9 @@ svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K,
  *                    separate calls.
  *  wq ... partials_debug   as for w4a8_linear / w8a8_linear.
  *
- *  For M = 1 (M <= 2 with 32-wide groups), K <= 12288 and block 32 this is
- *  ONE launch: every workgroup quantizes the row itself while its first
- *  weights are in flight.  Otherwise it enqueues the two launches.  Errors as for the two separate calls; N == 0 runs the
+ *  For M = 1 (M <= 2 with 32-wide groups) and K <= 12288 this is ONE launch:
+ *  every workgroup quantizes the row itself while its first weights are in
+ *  flight.  Otherwise it enqueues the two launches.  Errors as for the two separate calls; N == 0 runs the
  *  quantization alone.
  */
 svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,

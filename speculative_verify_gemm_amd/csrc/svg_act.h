@@ -188,7 +188,7 @@ SVG_DEV void wg_max_rows(float (&v)[R], float* red) {
 // LDS rows `out + r * stride` (words) and scales `scale[r]`: all loads issued
 // together and one reduction for all rows, so the latency is one row's.
 // Needs K <= 4 * NT * CPT; every thread of the workgroup must call it.
-template <int R, int CPT>
+template <int R, int CPT, int B = 32>
 SVG_DEV void act_quant_rows_lds(const float* X, int M, int K, const int8_t* signs, u32* out, int stride,
                                 float* scale, float* red) {
   RowRegs<CPT> rr[R];
@@ -196,11 +196,11 @@ SVG_DEV void act_quant_rows_lds(const float* X, int M, int K, const int8_t* sign
   for (int r = 0; r < R; ++r) act_load_row<CPT>(X + (size_t)r * K, r < M ? K : 0, signs, rr[r]);
   float amax[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) amax[r] = act_rotate_loaded<CPT>(rr[r]);
+  for (int r = 0; r < R; ++r) amax[r] = act_rotate_loaded<CPT, B>(rr[r]);
   wg_max_rows<R>(amax, red);
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    if (r < M) act_store_codes<CPT>(rr[r], K, amax[r], StoreLds{out + r * stride, scale + r});
+    if (r < M) act_store_codes<CPT, StoreLds, B>(rr[r], K, amax[r], StoreLds{out + r * stride, scale + r});
 }
 
 // Rotate (block B) and quantize row `x` (K values, K % B == 0); codes and the

@@ -15,8 +15,8 @@ hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* s
                                    uint16_t* w_scale, float* w_rot, hipStream_t stream);
 // The linears read int8 codes xq / x_scale; with X != nullptr they first
 // produce them from the fp32 rows X (signs, transform block), writing xq /
-// x_scale as outputs (inside the linear's own launch for M = 1 with the
-// 32-block, in a launch of their own before it otherwise).
+// x_scale as outputs (inside the linear's own launch for M = 1, in a launch
+// of their own before it otherwise).
 hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
                            float* y, int32_t* dbg, const float* X, const int8_t* signs, int block,

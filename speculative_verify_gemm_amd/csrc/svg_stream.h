@@ -32,6 +32,7 @@
 //   p.finish(t, slot)                reduce through LDS buffer `slot`, store, reset
 #pragma once
 #include <algorithm>
+#include <type_traits>
 
 #include "svg_act.h"
 #include "svg_device.h"
@@ -190,7 +191,7 @@ constexpr int fused_rows() { return P::kMaxTok <= 2 ? P::kMaxTok : 0; }
 struct ActIn {
   const float* X;
   const int8_t* signs;
-  int block;  // transform block; the fused kernel takes the pages' 32 only
+  int block;  // transform block, 32 or 64
 };
 
 template <class P, int WAVES, int CPW, int U>
@@ -225,16 +226,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
     // start of the whole weight stream waits for the rows.)
     for (int i = threadIdx.x; i < R * KP; i += blockDim.x)
       if (i / KP >= a.M || (i % KP) * 4 >= a.K) xl[i] = 0u;
-    if (row_early) {
-      const bool holds = (int)threadIdx.x < LT;
-      const float amax = wg_max(holds ? act_rotate_loaded<kLoadCPT>(early) : 0.f, act_red);
-      if (holds) act_store_codes<kLoadCPT>(early, a.K, amax, StoreLds{xl, xsl}, threadIdx.x, LT);
-    } else if (a.K <= 4 * CPT * (int)blockDim.x) {
-      act_quant_rows_lds<R, CPT>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
-    } else {
-      for (int m = 0; m < a.M; ++m)
-        act_quant_row<CPT>(f.X + (size_t)m * a.K, a.K, f.signs, StoreLds{xl + m * KP, xsl + m}, act_red);
-    }
+    // the transform block is uniform over the launch: both forms are in the
+    // kernel and one branch picks
+    auto quantize = [&](auto block) {
+      constexpr int B = decltype(block)::value;
+      if (row_early) {
+        const bool holds = (int)threadIdx.x < LT;
+        const float amax = wg_max(holds ? act_rotate_loaded<kLoadCPT, B>(early) : 0.f, act_red);
+        if (holds) act_store_codes<kLoadCPT, StoreLds, B>(early, a.K, amax, StoreLds{xl, xsl}, threadIdx.x, LT);
+      } else if (a.K <= 4 * CPT * (int)blockDim.x) {
+        act_quant_rows_lds<R, CPT, B>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
+      } else {
+        for (int m = 0; m < a.M; ++m)
+          act_quant_row<CPT, StoreLds, B>(f.X + (size_t)m * a.K, a.K, f.signs, StoreLds{xl + m * KP, xsl + m},
+                                          act_red);
+      }
+    };
+    if (f.block == 64) quantize(std::integral_constant<int, 64>{});
+    else quantize(std::integral_constant<int, 32>{});
     __syncthreads();
     if (blockIdx.x == 0) {  // the call's xq / x_scale outputs
       for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x) {
@@ -306,7 +315,7 @@ hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 template <class P>
 hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
-  if (f && (a.M > fused_rows<P>() || a.K > kLdsMaxK || f->block != 32)) {  // not fusable: quantize in a launch of their own
+  if (f && (a.M > fused_rows<P>() || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
     hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, f->block, const_cast<int8_t*>(a.xq),
                                             const_cast<float*>(a.x_scale), stream);
     if (e != hipSuccess) return e;

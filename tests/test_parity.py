@@ -399,7 +399,7 @@ def test_weight_codes_block64(fmt, group, N, K):
                                              ("w8", 0, 32, 40, 12288)])
 def test_linear_block64_end_to_end(fmt, group, M, N, K):
     """Weights and activations both rotated with 64-blocks, through the
-    fp32-input entry points (two launches for this block): codes, partial
+    fp32-input entry points (one launch at M = 1, two above): codes, partial
     sums and outputs against the oracle."""
     C.say(f"block=64 linear fmt={fmt} g={group} M={M} N={N} K={K}")
     x, W, signs = synth.random_case(M, N, K, seed=3 * M + N + K)
