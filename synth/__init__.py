@@ -234,6 +234,28 @@ def draft_tree(T: int, V: int, seed: int, shape: str = "bushy", accept: int | No
     return logits, parent, draft
 
 
+# ------------------------------------------------- recurrent layer on a tree
+def deltanet_case(T: int, H: int, d_k: int, d_v: int, seed: int, shape: str = "bushy"):
+    """Inputs of a gated delta-rule layer over a draft tree of T nodes and H
+    heads: (S0[H, d_v, d_k], q[T, H, d_k], k[T, H, d_k], v[T, H, d_v],
+    alpha[T, H], beta[T, H], parent[T]), fp32 / int32.
+
+    The tree shapes are those of draft_tree.  q, v ~ N(0, 1); keys N(0, 1)
+    scaled to unit length (the layer's keys are normalised); decay gates
+    alpha uniform in [0.9, 1); write strengths beta = sigmoid(N(0, 1)); the
+    live state S0 ~ N(0, 0.5)."""
+    rng = rng_for("test", seed, 8, "x")
+    _logits, parent, _draft = draft_tree(T, 2, seed, shape=shape)
+    q = rng.standard_normal((T, H, d_k), dtype=np.float32)
+    k = rng.standard_normal((T, H, d_k), dtype=np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True).astype(np.float32)
+    v = rng.standard_normal((T, H, d_v), dtype=np.float32)
+    alpha = rng.uniform(0.9, 1.0, size=(T, H)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    S0 = (0.5 * rng.standard_normal((H, d_v, d_k))).astype(np.float32)
+    return S0, q, k.astype(np.float32), v, alpha, beta, parent
+
+
 # -------------------------------------------------------------- device draws
 def stack_weight(layer: int, name: str, device="cuda"):
     """fp32 W[N, K] of one stack matrix, drawn with torch on `device`:
