@@ -268,6 +268,47 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
                               const int32_t* draft, int32_t* target, int32_t* path, int32_t* emit,
                               int32_t* n_emit, void* workspace, void* stream);
 
+/*
+ * tree_deltanet_verify, tree_deltanet_commit -- a fixed-state recurrent layer
+ * over a draft tree, without restoring state.
+ * [KT "Verifying a draft tree without restoring model state": a Gated
+ *  DeltaNet layer folds the past into a fixed-size state that every accepted
+ *  token changes; verification computes what every branch needs without
+ *  touching the live state, and only the accepted tokens' updates are applied
+ *  once the path is chosen.  The pages give no equations: the recurrence is
+ *  the gated delta rule of the Gated DeltaNet publication.]
+ *
+ *  Per head, a state S of dv x dk fp32 values; per token a query q and a key
+ *  k (dk values, the key of unit length), a value v (dv), a decay gate alpha
+ *  in (0, 1] and a write strength beta in [0, 1]:
+ *      S' = alpha * S (I - beta k k^T) + beta v k^T,     o = S' q.
+ *  The tree is that of tree_accept_greedy (node 0 the root, parent[i] < i);
+ *  the root is the last token of the sequence, not yet through the layer, so
+ *  node i's state is the live state advanced along its root path, root first.
+ *
+ *  state   fp32 [H][dv][dk], 16-byte aligned: the live state (verify reads
+ *          it only; commit updates it in place).
+ *  q, k    fp32 [T][H][dk], 16-byte aligned.     v  fp32 [T][H][dv].
+ *  alpha, beta  fp32 [T][H].                     parent  int32 [T].
+ *  out     OUTPUT fp32 [T][H][dv]: o of every node (verify).  A node whose
+ *          root path breaks the tree rule gets NaN.
+ *  path, n_emit  commit's accepted path as tree_accept_greedy wrote it: the
+ *          state advances by the root and path[0 .. n_emit - 2]; with
+ *          n_emit < 1 or a node outside [1, T) the state is left as it was.
+ *  T <= SVG_TREE_MAX_NODES; H >= 1; (dk, dv) in {(64, 64), (64, 128),
+ *  (128, 64), (128, 128), (64, 256)}.  fp32 arithmetic with fused
+ *  multiply-adds (the order of the sums differs from a plain loop: results
+ *  are close to an exact computation, not bit-identical to one).
+ *  One launch each.  Errors: SVG_EINVAL for a null pointer or T, H < 1;
+ *  SVG_EUNSUPPORTED for T > 32, H > 65535 or another head size; SVG_EALIGN.
+ */
+svg_status tree_deltanet_verify(const float* state, const float* q, const float* k, const float* v,
+                                const float* alpha, const float* beta, const int32_t* parent, int T,
+                                int H, int dk, int dv, float* out, void* stream);
+svg_status tree_deltanet_commit(float* state, const float* k, const float* v, const float* alpha,
+                                const float* beta, const int32_t* path, const int32_t* n_emit, int T,
+                                int H, int dk, int dv, void* stream);
+
 /* Text of the last error on the calling thread ("" after a successful call);
  * valid until the next call on this thread. */
 const char* svg_last_error(void);

@@ -5,7 +5,7 @@ shapes, derives the sizes, and calls the C entry point of the same name in
 libsvgemm.so on the current HIP stream (or the one given).  All computation
 runs in the library's HIP kernels; there is no Python or CPU fallback, and
 importing this module fails if the library has not been built
-(``python -m speculative_verify_gemm_amd.build``).
+(``python speculative_verify_gemm_amd/build.py``).
 
 The operations follow the page "Karpathy's Trick for Faster Local LLMs Finally
 Has Proper Tooling" (blog.dailydoseofds.com), section "How Uzu optimizes bytes
@@ -34,7 +34,7 @@ BLOCK = 32
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m speculative_verify_gemm_amd.build` (hipcc, gfx950)")
+                          "`python speculative_verify_gemm_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.rht_rotate_weights.argtypes = [vp, i, i, vp, i, i, i, vp, vp, vp, vp, vp]
@@ -44,8 +44,11 @@ def _load():
     lib.act_quant_w4a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.act_quant_w8a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, i, vp, vp, vp]
     lib.tree_accept_greedy.argtypes = [vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.tree_deltanet_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp]
+    lib.tree_deltanet_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
     for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear,
-               lib.act_quant_w4a8_linear, lib.act_quant_w8a8_linear, lib.tree_accept_greedy):
+               lib.act_quant_w4a8_linear, lib.act_quant_w8a8_linear, lib.tree_accept_greedy,
+               lib.tree_deltanet_verify, lib.tree_deltanet_commit):
         fn.restype = ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.svg_weight_sizes.argtypes = [i, i, i, i, u64p, u64p, u64p]
@@ -261,6 +264,42 @@ def tree_accept_greedy(logits, parent, draft, target, path, emit, n_emit, worksp
         raise ValueError("n_emit needs 1 element and workspace TREE_WORKSPACE_BYTES bytes")
     _check(lib.tree_accept_greedy(_p(logits), T, V, _p(parent), _p(draft), _p(target), _p(path),
                                   _p(emit), _p(n_emit), _p(workspace), _stream(stream, logits)))
+
+
+def _gdn_shapes(state, k, v, alpha, beta):
+    for name, t in (("state", state), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        _dev(t, name, torch.float32)
+    H, dv, dk = state.shape
+    T = k.shape[0]
+    if (tuple(k.shape) != (T, H, dk) or tuple(v.shape) != (T, H, dv) or tuple(alpha.shape) != (T, H)
+            or tuple(beta.shape) != (T, H)):
+        raise ValueError("need state [H, dv, dk], k [T, H, dk], v [T, H, dv], alpha and beta [T, H]")
+    return T, H, dk, dv
+
+
+def tree_deltanet_verify(state, q, k, v, alpha, beta, parent, out, stream=None):
+    """Outputs of a gated delta-rule layer at every node of a draft tree
+    (include/svgemm.h); `state` [H, dv, dk] is only read."""
+    T, H, dk, dv = _gdn_shapes(state, k, v, alpha, beta)
+    _dev(q, "q", torch.float32)
+    _dev(parent, "parent", torch.int32)
+    _dev(out, "out", torch.float32)
+    if tuple(q.shape) != (T, H, dk) or tuple(parent.shape) != (T,) or tuple(out.shape) != (T, H, dv):
+        raise ValueError("need q [T, H, dk], parent [T] and out [T, H, dv]")
+    _check(lib.tree_deltanet_verify(_p(state), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(parent),
+                                    T, H, dk, dv, _p(out), _stream(stream, state)))
+
+
+def tree_deltanet_commit(state, k, v, alpha, beta, path, n_emit, stream=None):
+    """Advance `state` in place by the root and the accepted path written by
+    tree_accept_greedy (path, n_emit)."""
+    T, H, dk, dv = _gdn_shapes(state, k, v, alpha, beta)
+    _dev(path, "path", torch.int32)
+    _dev(n_emit, "n_emit", torch.int32)
+    if path.numel() < T - 1 or n_emit.numel() < 1:
+        raise ValueError("path needs T - 1 entries and n_emit one")
+    _check(lib.tree_deltanet_commit(_p(state), _p(k), _p(v), _p(alpha), _p(beta), _p(path), _p(n_emit),
+                                    T, H, dk, dv, _stream(stream, state)))
 
 
 def empty_weights(N, K, fmt, group, device="cuda"):

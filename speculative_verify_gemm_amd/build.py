@@ -1,6 +1,6 @@
 """Build libsvgemm.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m speculative_verify_gemm_amd.build      # or: python speculative_verify_gemm_amd/build.py
+    python speculative_verify_gemm_amd/build.py      # (by path: the package itself loads the library)
 
 Every source is compiled with IEEE-exact fp32 settings (no FMA contraction,
 correctly rounded division, denormals kept) because the transform and the
@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsvgemm.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["rht_quant.hip", "linear_w4.hip", "linear_w8.hip", "tree_accept.hip", "svgemm.hip"]
+SOURCES = ["rht_quant.hip", "linear_w4.hip", "linear_w8.hip", "tree_accept.hip", "tree_deltanet.hip",
+           "svgemm.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

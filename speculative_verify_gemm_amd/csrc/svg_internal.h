@@ -31,6 +31,16 @@ hipError_t svg_launch_tree_accept(const float* logits, int T, int V, const int32
                                   int32_t* target, int32_t* path, int32_t* emit, int32_t* n_emit, void* workspace,
                                   hipStream_t stream);
 
+// Gated delta-rule layer over a draft tree (tree_deltanet.hip).  Head sizes:
+// d_k in {64, 128}, d_v in {64, 128, 256}, d_k * d_v <= 16384.
+bool svg_gdn_head_ok(int dk, int dv);
+hipError_t svg_launch_gdn_tree_verify(const float* state, const float* q, const float* k, const float* v,
+                                      const float* alpha, const float* beta, const int32_t* parent, int T, int H,
+                                      int dk, int dv, float* out, hipStream_t stream);
+hipError_t svg_launch_gdn_tree_commit(float* state, const float* k, const float* v, const float* alpha,
+                                      const float* beta, const int32_t* path, const int32_t* n_emit, int T, int H,
+                                      int dk, int dv, hipStream_t stream);
+
 // Bytes of the weight storage (include/svgemm.h describes the layout).
 // W4 codes: tiled, rows padded to 16 and K to 128.  Scales and zeros:
 // blocked per (16-row tile, 512-k block, row), rows padded to 16 and K to

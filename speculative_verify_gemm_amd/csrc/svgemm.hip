@@ -246,4 +246,35 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+svg_status tree_deltanet_verify(const float* state, const float* q, const float* k, const float* v,
+                                const float* alpha, const float* beta, const int32_t* parent, int T, int H,
+                                int dk, int dv, float* out, void* stream) {
+  static const char* fn = "tree_deltanet_verify";
+  if (!state || !q || !k || !v || !alpha || !beta || !parent || !out) return fail(SVG_EINVAL, fn, "null pointer");
+  if (T < 1 || H < 1) return fail(SVG_EINVAL, fn, "T and H must be >= 1");
+  if (T > SVG_TREE_MAX_NODES || H > 65535) return fail(SVG_EUNSUPPORTED, fn, "T > SVG_TREE_MAX_NODES or H > 65535");
+  if (!svg_gdn_head_ok(dk, dv)) return fail(SVG_EUNSUPPORTED, fn, "unsupported head size (dk, dv)");
+  if (!aligned(state, 16) || !aligned(q, 16) || !aligned(k, 16))
+    return fail(SVG_EALIGN, fn, "state, q and k need 16-byte alignment");
+  if (!aligned(v, 4) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(parent, 4) || !aligned(out, 4))
+    return fail(SVG_EALIGN, fn, "v, alpha, beta, parent and out need 4-byte alignment");
+  return hip_status(fn, svg_launch_gdn_tree_verify(state, q, k, v, alpha, beta, parent, T, H, dk, dv, out,
+                                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status tree_deltanet_commit(float* state, const float* k, const float* v, const float* alpha, const float* beta,
+                                const int32_t* path, const int32_t* n_emit, int T, int H, int dk, int dv,
+                                void* stream) {
+  static const char* fn = "tree_deltanet_commit";
+  if (!state || !k || !v || !alpha || !beta || !path || !n_emit) return fail(SVG_EINVAL, fn, "null pointer");
+  if (T < 1 || H < 1) return fail(SVG_EINVAL, fn, "T and H must be >= 1");
+  if (T > SVG_TREE_MAX_NODES || H > 65535) return fail(SVG_EUNSUPPORTED, fn, "T > SVG_TREE_MAX_NODES or H > 65535");
+  if (!svg_gdn_head_ok(dk, dv)) return fail(SVG_EUNSUPPORTED, fn, "unsupported head size (dk, dv)");
+  if (!aligned(state, 16) || !aligned(k, 16)) return fail(SVG_EALIGN, fn, "state and k need 16-byte alignment");
+  if (!aligned(v, 4) || !aligned(alpha, 4) || !aligned(beta, 4) || !aligned(path, 4) || !aligned(n_emit, 4))
+    return fail(SVG_EALIGN, fn, "v, alpha, beta, path and n_emit need 4-byte alignment");
+  return hip_status(fn, svg_launch_gdn_tree_commit(state, k, v, alpha, beta, path, n_emit, T, H, dk, dv,
+                                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -30,7 +30,8 @@ def svg():
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
         ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
-         "svg_last_error", "svg_weight_sizes", "tree_accept_greedy", "w4a8_linear", "w8a8_linear"])
+         "svg_last_error", "svg_weight_sizes", "tree_accept_greedy", "tree_deltanet_commit",
+         "tree_deltanet_verify", "w4a8_linear", "w8a8_linear"])
 
 
 def test_library_exports_every_declared_symbol(svg):
@@ -197,3 +198,37 @@ def _tree(svg, **kw):
 def test_tree_accept_validation(svg, kw, code):
     assert _tree(svg, **kw) == code
     assert svg.last_error().startswith("tree_accept_greedy:")
+
+
+def _gdn_verify(svg, **kw):
+    a = dict(state=A, q=A, k=A, v=A, alpha=A, beta=A, parent=A, T=4, H=2, dk=128, dv=128, out=A)
+    a.update(kw)
+    return svg.lib.tree_deltanet_verify(a["state"], a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["parent"],
+                                        a["T"], a["H"], a["dk"], a["dv"], a["out"], NULL)
+
+
+def _gdn_commit(svg, **kw):
+    a = dict(state=A, k=A, v=A, alpha=A, beta=A, path=A, n=A, T=4, H=2, dk=128, dv=128)
+    a.update(kw)
+    return svg.lib.tree_deltanet_commit(a["state"], a["k"], a["v"], a["alpha"], a["beta"], a["path"], a["n"],
+                                        a["T"], a["H"], a["dk"], a["dv"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=NULL), 1), (dict(q=NULL), 1), (dict(parent=NULL), 1), (dict(out=NULL), 1),
+    (dict(T=0), 1), (dict(H=0), 1),
+    (dict(T=33), 2), (dict(dk=96), 2), (dict(dk=128, dv=256), 2), (dict(dv=32), 2),
+    (dict(state=MIS), 3), (dict(k=ctypes.c_void_p(0x10004)), 3), (dict(out=MIS), 3),
+])
+def test_tree_deltanet_verify_validation(svg, kw, code):
+    assert _gdn_verify(svg, **kw) == code
+    assert svg.last_error().startswith("tree_deltanet_verify:")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=NULL), 1), (dict(path=NULL), 1), (dict(n=NULL), 1), (dict(T=0), 1),
+    (dict(T=40), 2), (dict(dk=32), 2), (dict(state=ctypes.c_void_p(0x10008)), 3), (dict(path=MIS), 3),
+])
+def test_tree_deltanet_commit_validation(svg, kw, code):
+    assert _gdn_commit(svg, **kw) == code
+    assert svg.last_error().startswith("tree_deltanet_commit:")
