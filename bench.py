@@ -373,6 +373,57 @@ def time_tree_accept(torch, dev, T, V, reps=50):
                 emitted_tokens=int(n.cpu()[0])), (logits, parent, draft)
 
 
+def time_tree_deltanet(torch, dev, T, H=16, dk=128, dv=128, reps=50):
+    """A gated delta-rule layer over a T-node draft tree (H heads of dk x dv
+    state): verification of every node, then the commit of a path, each timed
+    as back-to-back calls captured in a HIP graph."""
+    import numpy as np
+    import synth
+    import speculative_verify_gemm_amd as svg
+    S0, q, k, v, a, b, parent = synth.deltanet_case(T, H, dk, dv, seed=2026, shape="bushy")
+    Sd, qd, kd, vd, ad, bd = (torch.from_numpy(t).to(dev) for t in (S0, q, k, v, a, b))
+    pd = torch.from_numpy(parent.astype(np.int32)).to(dev)
+    out = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    path = torch.full((T,), -1, dtype=torch.int32, device=dev)
+    nodes, node = [], T - 1               # commit the root path of the last node
+    while node != 0:
+        nodes.append(node)
+        node = int(parent[node])
+    depth = len(nodes)
+    if depth:
+        path[:depth] = torch.tensor(nodes[::-1], dtype=torch.int32)
+    n_emit = torch.tensor([depth + 1], dtype=torch.int32, device=dev)
+    S_work = Sd.clone()
+
+    def timed(fn):
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e3 / (4 * reps)
+
+    us_v = timed(lambda: svg.tree_deltanet_verify(Sd, qd, kd, vd, ad, bd, pd, out))
+    us_c = timed(lambda: svg.tree_deltanet_commit(S_work, kd, vd, ad, bd, path, n_emit))
+    state_bytes = H * dv * dk * 4
+    return dict(T=T, H=H, dk=dk, dv=dv, verify_us=round(us_v, 3), commit_us=round(us_c, 3),
+                state_bytes=state_bytes, commit_path_len=depth,
+                verify_state_GB_per_s=round(state_bytes / (us_v * 1e-6) / 1e9, 2))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +548,11 @@ def main():
         print(f"[bench] tree acceptance T={tree['T']} V={tree['V']}: {tree['us_per_call']:.2f} us/call, "
               f"{tree['GB_per_s']:.1f} GB/s", file=sys.stderr, flush=True)
         out["tree_accept"] = tree
+    if args.tree_vocab:
+        dn = time_tree_deltanet(torch, dev, min(M, 32))
+        print(f"[bench] delta-rule tree T={dn['T']} H={dn['H']}: verify {dn['verify_us']:.2f} us, "
+              f"commit {dn['commit_us']:.2f} us", file=sys.stderr, flush=True)
+        out["tree_deltanet"] = dn
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
         cb = cpu_baseline(stack, M)

@@ -295,8 +295,7 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
  *  path, n_emit  commit's accepted path as tree_accept_greedy wrote it: the
  *          state advances by the root and path[0 .. n_emit - 2]; with
  *          n_emit < 1 or a node outside [1, T) the state is left as it was.
- *  T <= SVG_TREE_MAX_NODES; H >= 1; (dk, dv) in {(64, 64), (64, 128),
- *  (128, 64), (128, 128), (64, 256)}.  fp32 arithmetic with fused
+ *  T <= SVG_TREE_MAX_NODES; H >= 1; dk in {64, 128}, dv in {64, 128, 256}.  fp32 arithmetic with fused
  *  multiply-adds (the order of the sums differs from a plain loop: results
  *  are close to an exact computation, not bit-identical to one).
  *  One launch each.  Errors: SVG_EINVAL for a null pointer or T, H < 1;

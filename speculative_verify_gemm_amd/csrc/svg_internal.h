@@ -32,7 +32,7 @@ hipError_t svg_launch_tree_accept(const float* logits, int T, int V, const int32
                                   hipStream_t stream);
 
 // Gated delta-rule layer over a draft tree (tree_deltanet.hip).  Head sizes:
-// d_k in {64, 128}, d_v in {64, 128, 256}, d_k * d_v <= 16384.
+// d_k in {64, 128}, d_v in {64, 128, 256}.
 bool svg_gdn_head_ok(int dk, int dv);
 hipError_t svg_launch_gdn_tree_verify(const float* state, const float* q, const float* k, const float* v,
                                       const float* alpha, const float* beta, const int32_t* parent, int T, int H,

@@ -11,19 +11,21 @@
 // d_v x d_k values and, per token, S' = alpha S (I - beta k k^T) + beta v k^T
 // and o = S' q.
 //
-// Verification: one workgroup per (node, head) replays the node's root path
+// Verification: one workgroup per (node, head, row block) replays the node's root path
 // from the live state, which it only reads, and writes the node's output.
 // Nodes share no work, so the whole tree is one launch with no ordering
 // between workgroups; the replays cost (depth + 1) d_v d_k multiply-adds
 // each, which at the tree sizes of a verify pass (<= 32 nodes) is far below
-// the cost of reading the state.  Commit: one workgroup per head replays the
+// the cost of reading the state.  Commit: one workgroup per (head, row block) replays the
 // root and the accepted path (as the acceptance step wrote it) and stores the
 // state in place.
 //
-// Mapping: 256 threads; TPR = 256 / d_v threads share a state row, each
-// holding EPT = d_k / TPR consecutive values of it in registers for the
-// whole replay.  Row r's dot products with k and q are reduced across its TPR
-// consecutive lanes.
+// Mapping: the rows of a state evolve independently (row r only needs itself,
+// k and v[r]), so a head's d_v rows are split over d_v / 32 workgroups of 256
+// threads; 8 threads share a row, each holding d_k / 8 consecutive values in
+// registers for the whole replay, and a row's dot products with k and q are
+// reduced across its 8 consecutive lanes.  The path's tokens are staged in LDS first (one burst of
+// loads), so the replay is bound by arithmetic and LDS, not by memory latency.
 #include "svg_device.h"
 #include "svg_internal.h"
 
@@ -32,17 +34,21 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxNodes = 32;
 
+constexpr int kRowsPerGroup = 32;  // state rows per workgroup: rows evolve independently
+
 template <int DK, int DV>
 struct Layout {
-  static constexpr int TPR = kThreads / DV;  // threads per state row
-  static constexpr int EPT = DK / TPR;       // values per thread
-  static_assert(TPR >= 1 && kThreads % DV == 0 && DK % TPR == 0 && EPT % 4 == 0, "unsupported head size");
+  static constexpr int TPR = kThreads / kRowsPerGroup;  // threads per state row (8)
+  static constexpr int EPT = DK / TPR;                  // values per thread
+  static constexpr int GROUPS = DV / kRowsPerGroup;     // workgroups per head
+  static_assert(DV % kRowsPerGroup == 0 && DK % TPR == 0 && EPT % 4 == 0, "unsupported head size");
 };
 
 template <int TPR>
 SVG_DEV float row_sum(float v) {
   if constexpr (TPR >= 2) v += __shfl_xor(v, 1);
   if constexpr (TPR >= 4) v += __shfl_xor(v, 2);
+  if constexpr (TPR >= 8) v += __shfl_xor(v, 4);
   return v;
 }
 
@@ -66,6 +72,37 @@ SVG_DEV void gdn_advance(float (&S)[EPT], const float* __restrict__ k, float v_r
   for (int c = 0; c < EPT; ++c) S[c] = fmaf(w, kk[c], alpha * S[c]);
 }
 
+// The tokens of a path (this head's k, v, alpha, beta), staged in LDS by the
+// whole workgroup with all loads in flight at once: the replay then waits on
+// LDS only, not on one memory round trip per token.
+template <int DK, int DV>
+struct Tokens {
+  float k[kMaxNodes * DK];
+  float v[kMaxNodes * kRowsPerGroup];  // this workgroup's rows of each value
+  float a[kMaxNodes], b[kMaxNodes];
+};
+
+template <int DK, int DV>
+SVG_DEV void stage_tokens(const int* nodes, int len, const float* __restrict__ k, const float* __restrict__ v,
+                          const float* __restrict__ alpha, const float* __restrict__ beta, int H, int h,
+                          int row0, Tokens<DK, DV>& tok) {
+  for (int i = threadIdx.x; i < len * (DK / 4); i += kThreads) {
+    const int j = i / (DK / 4), c = i % (DK / 4);
+    reinterpret_cast<float4*>(tok.k)[i] =
+        reinterpret_cast<const float4*>(k + ((size_t)nodes[j] * H + h) * DK)[c];
+  }
+  for (int i = threadIdx.x; i < len * kRowsPerGroup; i += kThreads) {
+    const int j = i / kRowsPerGroup, c = i % kRowsPerGroup;
+    tok.v[i] = v[((size_t)nodes[j] * H + h) * DV + row0 + c];
+  }
+  if ((int)threadIdx.x < len) {
+    const size_t th = (size_t)nodes[threadIdx.x] * H + h;
+    tok.a[threadIdx.x] = alpha[th];
+    tok.b[threadIdx.x] = beta[th];
+  }
+  __syncthreads();
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void k_gdn_tree_verify(const float* __restrict__ state,
                                                              const float* __restrict__ q,
@@ -78,8 +115,9 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_verify(const float* __res
   using Lo = Layout<DK, DV>;
   __shared__ int path[kMaxNodes];
   __shared__ int len;
-  const int node = blockIdx.x, h = blockIdx.y;
-  const int r = threadIdx.x / Lo::TPR, c0 = (threadIdx.x % Lo::TPR) * Lo::EPT;
+  __shared__ Tokens<DK, DV> tok;
+  const int node = blockIdx.x, h = blockIdx.y, row0 = blockIdx.z * kRowsPerGroup;
+  const int rl = threadIdx.x / Lo::TPR, r = row0 + rl, c0 = (threadIdx.x % Lo::TPR) * Lo::EPT;
   if (threadIdx.x == 0) {  // the root path, root first; -1 if it is not a tree path
     int n = node, d = 0, ok = 1;
     int rev[kMaxNodes];
@@ -107,11 +145,9 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_verify(const float* __res
     const float4 t = *reinterpret_cast<const float4*>(s0 + c);
     S[c] = t.x; S[c + 1] = t.y; S[c + 2] = t.z; S[c + 3] = t.w;
   }
-  for (int j = 0; j < len; ++j) {
-    const int n = path[j];
-    const size_t th = (size_t)n * H + h;
-    gdn_advance<Lo::TPR, Lo::EPT>(S, k + th * DK, v[th * DV + r], alpha[th], beta[th], c0);
-  }
+  stage_tokens<DK, DV>(path, len, k, v, alpha, beta, H, h, row0, tok);
+  for (int j = 0; j < len; ++j)
+    gdn_advance<Lo::TPR, Lo::EPT>(S, tok.k + j * DK, tok.v[j * kRowsPerGroup + rl], tok.a[j], tok.b[j], c0);
   const float* qq = q + ((size_t)node * H) * DK + hd + c0;
   float o = 0.f;
 #pragma unroll
@@ -137,8 +173,9 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_commit(float* __restrict_
   using Lo = Layout<DK, DV>;
   __shared__ int nodes[kMaxNodes];
   __shared__ int len;
-  const int h = blockIdx.x;
-  const int r = threadIdx.x / Lo::TPR, c0 = (threadIdx.x % Lo::TPR) * Lo::EPT;
+  __shared__ Tokens<DK, DV> tok;
+  const int h = blockIdx.x, row0 = blockIdx.y * kRowsPerGroup;
+  const int rl = threadIdx.x / Lo::TPR, r = row0 + rl, c0 = (threadIdx.x % Lo::TPR) * Lo::EPT;
   if (threadIdx.x == 0) {  // root, then the accepted nodes; nothing if they are not valid nodes
     const int n = n_emit[0];
     int ok = n >= 1 && n <= T;
@@ -159,28 +196,26 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_commit(float* __restrict_
     const float4 t = *reinterpret_cast<const float4*>(s0 + c);
     S[c] = t.x; S[c + 1] = t.y; S[c + 2] = t.z; S[c + 3] = t.w;
   }
-  for (int j = 0; j < len; ++j) {
-    const size_t th = (size_t)nodes[j] * H + h;
-    gdn_advance<Lo::TPR, Lo::EPT>(S, k + th * DK, v[th * DV + r], alpha[th], beta[th], c0);
-  }
+  stage_tokens<DK, DV>(nodes, len, k, v, alpha, beta, H, h, row0, tok);
+  for (int j = 0; j < len; ++j)
+    gdn_advance<Lo::TPR, Lo::EPT>(S, tok.k + j * DK, tok.v[j * kRowsPerGroup + rl], tok.a[j], tok.b[j], c0);
 #pragma unroll
   for (int c = 0; c < Lo::EPT; c += 4) *reinterpret_cast<float4*>(s0 + c) = make_float4(S[c], S[c + 1], S[c + 2], S[c + 3]);
 }
 
 }  // namespace
 
-bool svg_gdn_head_ok(int dk, int dv) {
-  return (dk == 64 || dk == 128) && (dv == 64 || dv == 128 || dv == 256) && dk * dv <= 16384;
-}
+bool svg_gdn_head_ok(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128 || dv == 256); }
 
-#define SVG_GDN_SHAPES(X) X(64, 64) X(64, 128) X(128, 64) X(128, 128) X(64, 256)
+#define SVG_GDN_SHAPES(X) X(64, 64) X(64, 128) X(64, 256) X(128, 64) X(128, 128) X(128, 256)
 
 hipError_t svg_launch_gdn_tree_verify(const float* state, const float* q, const float* k, const float* v,
                                       const float* alpha, const float* beta, const int32_t* parent, int T, int H,
                                       int dk, int dv, float* out, hipStream_t stream) {
 #define SVG_GDN_V(DK, DV)                                                                                      \
   if (dk == DK && dv == DV) {                                                                                  \
-    hipLaunchKernelGGL((k_gdn_tree_verify<DK, DV>), dim3(T, H), dim3(kThreads), 0, stream, state, q, k, v,     \
+    hipLaunchKernelGGL((k_gdn_tree_verify<DK, DV>), dim3(T, H, DV / kRowsPerGroup), dim3(kThreads), 0, stream, \
+                       state, q, k, v,                                                                         \
                        alpha, beta, parent, T, H, out);                                                        \
     return hipGetLastError();                                                                                  \
   }
@@ -194,7 +229,8 @@ hipError_t svg_launch_gdn_tree_commit(float* state, const float* k, const float*
                                       int dk, int dv, hipStream_t stream) {
 #define SVG_GDN_C(DK, DV)                                                                                      \
   if (dk == DK && dv == DV) {                                                                                  \
-    hipLaunchKernelGGL((k_gdn_tree_commit<DK, DV>), dim3(H), dim3(kThreads), 0, stream, state, k, v, alpha,    \
+    hipLaunchKernelGGL((k_gdn_tree_commit<DK, DV>), dim3(H, DV / kRowsPerGroup), dim3(kThreads), 0, stream,   \
+                       state, k, v, alpha,                                                                     \
                        beta, path, n_emit, T, H);                                                              \
     return hipGetLastError();                                                                                  \
   }

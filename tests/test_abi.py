@@ -217,7 +217,7 @@ def _gdn_commit(svg, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(state=NULL), 1), (dict(q=NULL), 1), (dict(parent=NULL), 1), (dict(out=NULL), 1),
     (dict(T=0), 1), (dict(H=0), 1),
-    (dict(T=33), 2), (dict(dk=96), 2), (dict(dk=128, dv=256), 2), (dict(dv=32), 2),
+    (dict(T=33), 2), (dict(dk=96), 2), (dict(dk=128, dv=512), 2), (dict(dv=32), 2),
     (dict(state=MIS), 3), (dict(k=ctypes.c_void_p(0x10004)), 3), (dict(out=MIS), 3),
 ])
 def test_tree_deltanet_verify_validation(svg, kw, code):

@@ -53,7 +53,7 @@ def dev(case):
 CASES = [  # T, H, dk, dv, tree shape
     (1, 1, 128, 128, "chain"), (16, 16, 128, 128, "bushy"), (32, 4, 128, 128, "chain"),
     (9, 3, 64, 64, "star"), (12, 2, 64, 128, "bushy"), (7, 5, 128, 64, "bushy"), (5, 2, 64, 256, "chain"),
-    (32, 2, 64, 64, "bushy"),
+    (32, 2, 64, 64, "bushy"), (10, 3, 128, 256, "bushy"),
 ]
 
 
