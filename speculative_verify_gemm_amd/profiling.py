@@ -90,8 +90,12 @@ def trace_summary(d, cmd, only=None):
         if not n.startswith(only or "k_"):
             other.append(dur)
             continue
-        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
-        by.setdefault((n, wgs, int(r["Workgroup_Size_X"])), []).append(dur)
+        wgs, wg = 1, 1
+        for ax in ("X", "Y", "Z"):  # grid sizes are in threads, per dimension
+            g, w = int(r.get(f"Grid_Size_{ax}") or 1), max(1, int(r.get(f"Workgroup_Size_{ax}") or 1))
+            wgs *= max(1, g // w)
+            wg *= w
+        by.setdefault((n, wgs, wg), []).append(dur)
     lines = ["# rocprofv3 kernel trace", "", "Command:", "", "```", cmd, "```", "",
              "Durations are kernel-trace spans (start to end of each dispatch).", "",
              "| kernel | workgroups x threads | dispatches | mean us | median us | min us |",
