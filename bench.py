@@ -200,7 +200,7 @@ def time_graph(torch, g, steps, warmup, dev):
     return ev[0].elapsed_time(ev[-1]) / steps, per[len(per) // 2], per[0]
 
 
-def time_linear_launches(stack, io, g, ms_graph, steps):
+def time_linear_launches(stack, io, g, ms_graph, steps, unfused=False):
     """Mean duration of the linear kernel's launches, from HIP events recorded
     on the stream they run on.  For each launch kind of a layer (qkv, o,
     gate/up, down) the launches of all layers run back to back between two
@@ -212,9 +212,10 @@ def time_linear_launches(stack, io, g, ms_graph, steps):
     quantized once before, untimed.  Before each step the captured pass is replayed enough
     times to keep the device busy while the host enqueues, so no host launch
     latency enters the timed spans.
+    With `unfused` the linear alone is timed at every M.
     Returns (mean ms, mean algorithmic bytes, launches, {kind: mean us})."""
     torch = stack.torch
-    fused = stack.fused and one_launch(io["M"], stack.group)
+    fused = stack.fused and one_launch(io["M"], stack.group) and not unfused
     t0 = time.perf_counter()
     stack.run_pass(io)                       # host cost of enqueuing one eager pass
     enqueue_ms = (time.perf_counter() - t0) * 1e3
@@ -533,6 +534,15 @@ def main():
                             "frac_of_hbm_peak": round(nbytes1 / (ms1 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                             "bytes_per_pass": nbytes1}
         out[f"verify_m{M}_over_decode_m1"] = round(ms / ms1, 4)
+        # the contraction alone, both M on activations quantized beforehand: what
+        # the pass costs when the quantization rides in the producer of the
+        # activations (a norm or activation kernel in a whole model)
+        _k1, _b1, _n1, kmed1 = time_linear_launches(stack, _io1, g1, ms1, max(1, min(args.steps, 5)), unfused=True)
+        t16, t1 = sum(kmed.values()), sum(kmed1.values())
+        out["linear_only_per_layer"] = {"us_m1": round(t1, 3), f"us_m{M}": round(t16, 3),
+                                        "ratio": round(t16 / t1, 4), "m1_by_kind": kmed1}
+        print(f"[bench] linears alone per layer: M=1 {t1:.2f} us, M={M} {t16:.2f} us (x{t16 / t1:.3f})",
+              file=sys.stderr, flush=True)
         del g1
     if args.sweep:
         rows = []
