@@ -50,7 +50,8 @@ typedef int svg_status;
 enum {
     SVG_OK = 0,
     SVG_EINVAL = 1,        /* null required pointer, negative size, K <= 0      */
-    SVG_EUNSUPPORTED = 2,  /* block not 32 or 64, K % 32, K % block, K % group, group not in
+    SVG_EUNSUPPORTED = 2,  /* K > 2^24, a weight array of 4 GiB or more,
+                              block not 32 or 64, K % 32, K % block, K % group, group not in
                               {32, 64, 128}, M > 32, unknown fmt, W8 K > 131072 */
     SVG_EALIGN = 3,        /* a pointer below its required alignment          */
     SVG_EHIP = 4           /* a HIP launch or runtime error (text in
@@ -260,8 +261,8 @@ svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* sig
  *  One launch: the logits stream once (T * V * 4 bytes); the workgroup that
  *  finishes last reads the row maxima and walks the tree.
  *  Errors: SVG_EINVAL for a null pointer, T < 1 or V < 1; SVG_EUNSUPPORTED for
- *  T > SVG_TREE_MAX_NODES; SVG_EALIGN for logits not 4-byte or workspace not
- *  8-byte aligned.
+ *  T > SVG_TREE_MAX_NODES or V > 2^30; SVG_EALIGN for logits not 4-byte or
+ *  workspace not 8-byte aligned.
  */
 enum { SVG_TREE_MAX_NODES = 32, SVG_TREE_WORKSPACE_BYTES = 512 };
 svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* parent,

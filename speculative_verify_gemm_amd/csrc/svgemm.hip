@@ -41,6 +41,21 @@ bool block_ok(int b) { return b == 32 || b == 64; }
 
 constexpr int kMaxM = 32;
 constexpr int kMaxKW8 = 131072;  // 127^2 * K < 2^31
+constexpr int kMaxK = 1 << 24;   // row offsets of the activation buffers stay 32-bit
+constexpr int kMaxV = 1 << 30;   // vocabulary of the tree acceptance (slice arithmetic in int)
+
+// The kernels address each weight array through one buffer resource (32-bit
+// byte range): a matrix whose codes, scales or zeros reach 4 GiB is refused.
+bool fits_w4(int N, int K, int group, bool z4) {
+  size_t w, s, z;
+  svg_w4_storage(N, K, group, z4, &w, &s, &z);
+  return w < (1ull << 32) && s < (1ull << 32) && z < (1ull << 32);
+}
+bool fits_w8(int N, int K) {
+  size_t w, s;
+  svg_w8_storage(N, K, &w, &s);
+  return w < (1ull << 32) && s < (1ull << 32);
+}
 
 }  // namespace
 
@@ -96,6 +111,9 @@ svg_status rht_rotate_weights(const float* W, int N, int K, const int8_t* signs,
   const bool w4 = fmt != SVG_W8_SYM;
   if (w4 && !group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
   if (w4 && K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of group");
+  if (K > kMaxK) return fail(SVG_EUNSUPPORTED, fn, "K > 2^24");
+  if (w4 ? !fits_w4(N, K, group, fmt == SVG_W4_ASYM_Z4) : !fits_w8(N, K))
+    return fail(SVG_EUNSUPPORTED, fn, "weight storage of 4 GiB or more: split the matrix along N");
   if (!W || !signs || !wq || !w_scale || (w4 && !w_zero))
     return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(W, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "W and wq need 16-byte alignment");
@@ -122,6 +140,7 @@ svg_status act_rht_quant_i8(const float* X, int M, int K, const int8_t* signs, i
   if (!block_ok(block)) return fail(SVG_EUNSUPPORTED, fn, "block must be 32 or 64");
   if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
   if (K % block) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of block");
+  if (K > kMaxK) return fail(SVG_EUNSUPPORTED, fn, "K > 2^24");
   if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
   if (!X || !signs || !xq || !x_scale) return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(X, 16) || !aligned(xq, 16)) return fail(SVG_EALIGN, fn, "X and xq need 16-byte alignment");
@@ -143,6 +162,9 @@ svg_status check_w4(const char* fn, const int8_t* xq, const float* x_scale, int 
   if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16) return fail(SVG_EUNSUPPORTED, fn, "fmt must be a W4 format");
   if (!group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
   if (K % 32 || K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32 and of group");
+  if (K > kMaxK) return fail(SVG_EUNSUPPORTED, fn, "K > 2^24");
+  if (!fits_w4(N, K, group, fmt == SVG_W4_ASYM_Z4))
+    return fail(SVG_EUNSUPPORTED, fn, "weight storage of 4 GiB or more: split the matrix along N");
   if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
   if (!xq || !x_scale || !wq || !w_scale || !w_zero || !y) return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "xq and wq need 16-byte alignment");
@@ -158,6 +180,7 @@ svg_status check_w8(const char* fn, const int8_t* xq, const float* x_scale, int 
   if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
   if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
   if (K > kMaxKW8) return fail(SVG_EUNSUPPORTED, fn, "K > 131072 would overflow int32 partial sums");
+  if (!fits_w8(N, K)) return fail(SVG_EUNSUPPORTED, fn, "weight storage of 4 GiB or more: split the matrix along N");
   if (M > kMaxM) return fail(SVG_EUNSUPPORTED, fn, "M > 32");
   if (!xq || !x_scale || !wq || !w_scale || !y) return fail(SVG_EINVAL, fn, "null required pointer");
   if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(SVG_EALIGN, fn, "xq and wq need 16-byte alignment");
@@ -240,6 +263,7 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
     return fail(SVG_EINVAL, fn, "null pointer");
   if (T < 1 || V < 1) return fail(SVG_EINVAL, fn, "T and V must be >= 1");
   if (T > SVG_TREE_MAX_NODES) return fail(SVG_EUNSUPPORTED, fn, "T > SVG_TREE_MAX_NODES");
+  if (V > kMaxV) return fail(SVG_EUNSUPPORTED, fn, "V > 2^30");
   if (!aligned(logits, 4)) return fail(SVG_EALIGN, fn, "logits must be 4-byte aligned");
   if (!aligned(workspace, 8)) return fail(SVG_EALIGN, fn, "workspace must be 8-byte aligned");
   return hip_status(fn, svg_launch_tree_accept(logits, T, V, parent, draft, target, path, emit, n_emit, workspace,

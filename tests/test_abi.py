@@ -232,3 +232,12 @@ def test_tree_deltanet_verify_validation(svg, kw, code):
 def test_tree_deltanet_commit_validation(svg, kw, code):
     assert _gdn_commit(svg, **kw) == code
     assert svg.last_error().startswith("tree_deltanet_commit:")
+
+
+def test_size_limits_are_refused(svg):
+    # K beyond 2^24, and weight storage of 4 GiB or more (one buffer range)
+    assert _w4(svg, K=(1 << 24) + 128, g=64) == 2
+    assert svg.lib.w8a8_linear(A, A, 1, 131072, A, A, 1 << 19, A, NULL, NULL) == 2   # 64 GiB of codes
+    assert _w4(svg, N=1 << 21, K=8192, g=64) == 2                                     # 8 GiB of codes
+    assert svg.lib.rht_rotate_weights(A, 1 << 21, 8192, A, 32, 1, 64, A, A, A, NULL, NULL) == 2
+    assert _tree(svg, V=(1 << 30) + 1) == 2
