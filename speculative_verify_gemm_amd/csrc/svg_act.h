@@ -19,7 +19,8 @@
 // rounded) followed by round-half-to-even gives.  Dividing is slow, so the
 // quotient is first estimated as t = u * (1 / sigma): |t - u/sigma| <= 2^-16
 // for |u/sigma| <= 128, and the correctly rounded quotient is within 2^-18 of
-// u/sigma.  Unless t lies within 2^-13 of a half-integer, both round to the
+// u/sigma.  Unless t lies within 2^-13 of a half-integer -- that is, unless
+// |t - rint(t)| >= 1/2 - 2^-13 (t - rint(t) is exact) -- both round to the
 // same integer as t, so rint(t) is the code; near a half-integer (about one
 // value in 4000) the exact division decides.
 #pragma once
@@ -29,15 +30,28 @@
 
 SVG_DEV int clamp_i(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// int8 code of u for the scale sigma (> 0); rinv = 1 / sigma; `fast` is false
-// when 1 / sigma is not a normal float (then every code divides).
-SVG_DEV int act_code(float u, float sigma, float rinv, bool fast) {
-  if (fast) {
-    const float t = u * rinv;
-    const float f = t - floorf(t);  // exact
-    if (fabsf(f - 0.5f) > 0x1p-13f) return clamp_i((int)rintf(t), -127, 127);
+// int8 codes of four values u for the scale sigma (> 0); rinv = 1 / sigma;
+// `fast` is false when 1 / sigma is not a normal float (then every code
+// divides).  The exact divisions sit behind one wave-uniform branch, taken
+// only when some lane of the wave needs one: a per-lane branch is flattened
+// by the compiler, and every value would then pay for the division.
+SVG_DEV void act_codes4(const float u[4], float sigma, float rinv, bool fast, int q[4]) {
+  float r[4];
+  bool exact[4], any = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = u[i] * rinv;
+    r[i] = rintf(t);
+    exact[i] = !fast || !(fabsf(t - r[i]) < 0.5f - 0x1p-13f);
+    any = any || exact[i];
   }
-  return clamp_i((int)rintf(u / sigma), -127, 127);
+  if (__any(any)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (exact[i]) r[i] = rintf(u[i] / sigma);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = clamp_i((int)r[i], -127, 127);
 }
 
 // Max over the workgroup (exact: max is order-free).  red: >= 16 floats of LDS.
@@ -146,10 +160,7 @@ SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Sto
     const u32 c = tid + NT * i;
     if (c < nchunk) {
       int q[4] = {0, 0, 0, 0};
-      if (amax > 0.f) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) q[t] = act_code(r.e[i][t], sigma, rinv, fast);
-      }
+      if (amax > 0.f) act_codes4(r.e[i], sigma, rinv, fast, q);
       st.word(c, pack4(q));
     }
   }
@@ -233,10 +244,7 @@ SVG_DEV void act_quant_row(const float* x, int K, const int8_t* signs, const Sto
     float e[4];
     act_rotate4<B>(xr, sr, c, e);
     int q[4] = {0, 0, 0, 0};
-    if (amax > 0.f) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) q[t] = act_code(e[t], sigma, rinv, fast);
-    }
+    if (amax > 0.f) act_codes4(e, sigma, rinv, fast, q);
     st.word(c, pack4(q));
   }
 }
