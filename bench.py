@@ -201,8 +201,9 @@ def time_graph(torch, g, steps, warmup, dev):
 
 
 def time_linear_launches(stack, io, g, ms_graph, steps, unfused=False):
-    """Mean duration of the linear kernel's launches, from HIP events recorded
-    on the stream they run on.  For each launch kind of a layer (qkv, o,
+    """Duration of the linear kernel's launches, from HIP events recorded on
+    the stream they run on (per kind, the median over `steps` of the mean
+    launch time of a step).  For each launch kind of a layer (qkv, o,
     gate/up, down) the launches of all layers run back to back between two
     events, so the event overhead spreads over `layers` launches and each
     launch counts from the end of the previous one to its own end -- the span
@@ -238,7 +239,9 @@ def time_linear_launches(stack, io, g, ms_graph, steps, unfused=False):
         torch.cuda.synchronize(stack.dev)
         for name, e0, e1 in spans:
             per_kind[name].append(e0.elapsed_time(e1) / stack.layers)
-    mean_kind = {n: sum(v) / len(v) for n, v in per_kind.items()}
+    # per kind, the median over steps of the mean launch time of a step (one
+    # disturbed step -- a clock or power transition -- does not move it)
+    mean_kind = {n: sorted(v)[len(v) // 2] for n, v in per_kind.items()}
     mean_ms = sum(mean_kind.values()) / len(mean_kind)
     nbytes = [linear_bytes(io["M"], N, K, stack.fmt, stack.group) for _n, _m, N, K, _s in LAYER_LAUNCHES]
     return (mean_ms, sum(nbytes) / len(nbytes), steps * stack.layers * len(LAYER_LAUNCHES),
@@ -480,7 +483,7 @@ def main():
 
     io, g, (ms, ms_med, ms_min), nbytes = measure(M)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    kmean_ms, kbytes, nlaunch, kmed = time_linear_launches(stack, io, g, ms, max(1, min(args.steps, 5)))
+    kmean_ms, kbytes, nlaunch, kmed = time_linear_launches(stack, io, g, ms, max(1, min(args.steps, 7)))
     k_gbps = kbytes / (kmean_ms * 1e-3) / 1e9
     print(f"[bench] linear launches: mean {kmean_ms * 1e3:.2f} us, {k_gbps:.1f} GB/s; per kind us {kmed}",
           file=sys.stderr, flush=True)
@@ -537,7 +540,7 @@ def main():
         # the contraction alone, both M on activations quantized beforehand: what
         # the pass costs when the quantization rides in the producer of the
         # activations (a norm or activation kernel in a whole model)
-        _k1, _b1, _n1, kmed1 = time_linear_launches(stack, _io1, g1, ms1, max(1, min(args.steps, 5)), unfused=True)
+        _k1, _b1, _n1, kmed1 = time_linear_launches(stack, _io1, g1, ms1, max(1, min(args.steps, 7)), unfused=True)
         t16, t1 = sum(kmed.values()), sum(kmed1.values())
         out["linear_only_per_layer"] = {"us_m1": round(t1, 3), f"us_m{M}": round(t16, 3),
                                         "ratio": round(t16 / t1, 4), "m1_by_kind": kmed1}
