@@ -18,13 +18,14 @@
 // that (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) are the codes of k..k+3
 // and k+4..k+7 in natural order.  Activations therefore need no reordering.
 //
-//  * MfmaW4 (M > 2, g = 64 or 128): MFMA 1 takes the first run of every
+//  * MfmaW4 (M >= 2, g = 64 or 128): MFMA 1 takes the first run of every
 //    lane (k 0..63 of the chunk), MFMA 2 the second (k 64..127).  For g = 64
 //    each is exactly one quantization group; a second MFMA of the same
 //    activations against a B holding -z in every byte accumulates
 //    -z * sum_{k in g} xq[m][k] onto it, which closes S_g exactly with no
 //    vector arithmetic.  For g = 128 all four MFMAs chain into one group.
-//  * DotW4 (M <= 2, and g = 32 at any M): v_dot4_i32_i8 on the same
+//  * DotW4 (M = 1, and g = 32 at any M -- up to 2 tokens per launch, or 8
+//    per launch after a separate quantization): v_dot4_i32_i8 on the same
 //    tiles, lane (r, b) owning its two 16-k runs of row r.
 //
 // Workgroups are persistent (svg_stream.h): each walks 16-row tiles, its

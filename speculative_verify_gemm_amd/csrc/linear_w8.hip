@@ -13,8 +13,8 @@
 // integer sum closes once per row, so both kernels accumulate int32 across the
 // whole K range and apply the two scales once at the end:
 //
-//  * DotW8  (M <= 2): v_dot4_i32_i8 on the tiles.
-//  * MfmaW8 (M > 2): v_mfma_i32_16x16x64_i8 chained over K; A = 16
+//  * DotW8  (M = 1): v_dot4_i32_i8 on the tiles.
+//  * MfmaW8 (M >= 2; two 16-token halves above 16): v_mfma_i32_16x16x64_i8 chained over K; A = 16
 //    tokens x 64 k, B = 64 k x 16 rows, both in natural k order.
 //
 // Workgroups walk the 16-row tiles persistently (svg_stream.h): waves own

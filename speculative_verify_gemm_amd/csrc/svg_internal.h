@@ -63,6 +63,7 @@ inline void svg_w8_storage(int N, int K, size_t* wq_bytes, size_t* scale_bytes) 
 // Compute units of the current device (cached per device id).
 int svg_cu_count();
 
-// The dot-product (GEMV) kernels serve M = 1 (and M <= 2 for 32-wide groups,
-// which have no MFMA form); larger M use MFMA, whose matrix pipe is otherwise
+// The dot-product (GEMV) kernels serve M = 1, and every M with 32-wide groups
+// (which have no MFMA form: two tokens per launch, or eight per launch after a
+// separate quantization); larger M use MFMA, whose matrix pipe is otherwise
 // idle, with the rows past M zero.
