@@ -54,6 +54,19 @@ SVG_DEV void act_codes4(const float u[4], float sigma, float rinv, bool fast, in
   for (int i = 0; i < 4; ++i) q[i] = clamp_i((int)r[i], -127, 127);
 }
 
+// Max over the workgroup with one barrier, for a `red` (>= 16 floats of LDS)
+// that no earlier code of the kernel reads.
+SVG_DEV float wg_max_once(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < nw; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
 // Max over the workgroup (exact: max is order-free).  red: >= 16 floats of LDS.
 SVG_DEV float wg_max(float v, float* red) {
 #pragma unroll

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
       constexpr int B = decltype(block)::value;
       if (row_early) {
         const bool holds = (int)threadIdx.x < LT;
-        const float amax = wg_max(holds ? act_rotate_loaded<kLoadCPT, B>(early) : 0.f, act_red);
+        const float amax = wg_max_once(holds ? act_rotate_loaded<kLoadCPT, B>(early) : 0.f, act_red);
         if (holds) act_store_codes<kLoadCPT, StoreLds, B>(early, a.K, amax, StoreLds{xl, xsl}, threadIdx.x, LT);
       } else if (a.K <= 4 * CPT * (int)blockDim.x) {
         act_quant_rows_lds<R, CPT, B>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
