@@ -67,6 +67,7 @@ SVG_DEV v4i as_v4i(u32x4 a) { return v4i{(int)a[0], (int)a[1], (int)a[2], (int)a
 // batch is one aligned load per array; padding holds scale 0 and zero 0.
 template <int GPC, bool Z4, int U>
 struct GroupParams {
+  static_assert(U == 1 || U == 2 || U == 4, "a batch must lie inside one 512-k parameter block");
   static constexpr int NV = U * GPC;                  // values in the batch
   static constexpr int GPB = 4 * GPC;                 // values per (block, row)
   static constexpr int SBY = 2 * NV;                  // scale bytes
