@@ -315,7 +315,8 @@ def test_fused_in_captured_graph():
 STACK_CASES = [("stack_w4g64", 16, "qkv"), ("stack_w4g64", 16, "down"), ("stack_w4g64", 1, "gateup"),
                ("stack_w4g64", 1, "down"), ("stack_w8", 32, "qkv"), ("stack_w8", 32, "down"),
                ("stack_w8", 1, "o"), ("stack_w4g128", 32, "down"), ("stack_w4g128", 32, "gateup"),
-               ("stack_w4g128", 1, "qkv"), ("stack_w4g128", 4, "down"), ("stack_w4g128", 8, "o")]
+               ("stack_w4g128", 1, "qkv"), ("stack_w4g128", 2, "gateup"), ("stack_w4g128", 4, "down"),
+               ("stack_w4g128", 8, "o"), ("stack_w4g128", 16, "qkv")]
 
 
 @pytest.mark.parametrize("workload,M,launch", STACK_CASES)
