@@ -526,6 +526,7 @@ def main():
                      "mean_launch_us_by_kind": kmed,
                      "mean_algorithmic_bytes_per_launch": round(kbytes),
                      "launches_timed": nlaunch,
+                     "mean_algorithmic_int8_ops_per_launch": round(kops),
                      "int8_tops_pass": round(ops_per_pass / (ms * 1e-3) / 1e12, 2),
                      "int8_tops_kernel": round(kops / (kmean_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_kernel": round(kops / (kmean_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)},
@@ -541,6 +542,10 @@ def main():
         # the pass costs when the quantization rides in the producer of the
         # activations (a norm or activation kernel in a whole model)
         _k1, _b1, _n1, kmed1 = time_linear_launches(stack, _io1, g1, ms1, max(1, min(args.steps, 7)), unfused=True)
+        traffic1, traffic1_src = profiled_traffic(args.workload, 1)
+        out["decode_m1"]["traffic"] = {"bytes_per_launch": round(traffic1) if traffic1 else None,
+                                       "source": traffic1_src,
+                                       "algorithmic_bytes_per_launch": round(_b1)}
         t16, t1 = sum(kmed.values()), sum(kmed1.values())
         out["linear_only_per_layer"] = {"us_m1": round(t1, 3), f"us_m{M}": round(t16, 3),
                                         "ratio": round(t16 / t1, 4), "m1_by_kind": kmed1}

@@ -1,6 +1,7 @@
 """Short text summaries of rocprofv3 runs of bench.py, for profiles/.
 
     python -m speculative_verify_gemm_amd.profiling trace <trace dir> --cmd "<command>" --out <file.md>
+    python -m speculative_verify_gemm_amd.profiling mfma <pmc dir>=<bench out> ... --cmd "<commands>" --out <file.md>
     python -m speculative_verify_gemm_amd.profiling traffic <fetch dir> <write dir> --calib-mib 256 \\
         --workload stack_w4g64 --m 16 --fetch-json <bench out> --write-json <bench out> \\
         --cmd "<commands>" --out <file.md>
@@ -8,6 +9,14 @@
 `trace` reads the kernel trace (`--kernel-trace`, csv) and lists every kernel's
 dispatch count and mean / median / min duration, with the W4A8 and W8A8 linear
 kernels also pooled over the launch mix of a pass.
+
+`mfma` reads counter runs of the MFMA passes (`--pmc MfmaUtil
+SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_INSTS_VALU_MFMA_I8`, one run per workload and
+M), each paired with the bench.py line of a plain run (no profiler: counter
+collection serializes the dispatches) of the same workload and M, and lists
+per linear kernel the share of SIMD cycles the matrix unit was busy, the int8
+operations it executed per launch against the algorithmic 2*M*N*K, and the
+executed rate over the plain run's mean launch duration.
 
 `traffic` reads two counter runs (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`):
 each counter is scaled by what it reads for the device-to-device copy of
@@ -177,6 +186,63 @@ def traffic_summary(fetch_dir, write_dir, calib_mib, workload, M, cmd, fetch_jso
     return "\n".join(lines)
 
 
+PEAK_I8_TOPS = 5000.0  # MI355X dense int8 MFMA, TOP/s
+
+
+def _bench_line(path):
+    import json
+    with open(path) as f:
+        lines = [ln for ln in f if ln.startswith("{")]
+    if not lines:
+        raise SystemExit(f"no bench JSON line in {path}")
+    return json.loads(lines[-1])
+
+
+def mfma_summary(runs, cmd):
+    """runs: [(counter dir, bench.py output of a plain run)], one per workload
+    and M."""
+    lines = ["# rocprofv3 MFMA counters of the linear kernels", "", "Commands (one counter run per row group):", "",
+             "```", cmd, "```", "",
+             "Per linear kernel of each run: `busy` = MfmaUtil, the matrix unit's busy cycles over all SIMDs "
+             "divided by (GPU-active cycles x SIMDs) during the dispatch, so launch ramp and tail count as idle; "
+             "`executed` = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512 int8 operations per launch; `algorithmic` = "
+             "2*M*N*K per launch (the MFMA form executes more: rows padded to 16 tokens, the zero-point "
+             "MFMA of W4); `rate` = executed operations over the mean linear launch duration of a plain "
+             f"32-layer run (bench.py, HIP events), against the {PEAK_I8_TOPS:.0f} TOP/s dense int8 peak.", "",
+             "| workload | M | kernel | dispatches | busy % | MFMA instr / launch | executed Gop / launch | "
+             "algorithmic Gop / launch | executed / algorithmic | mean launch us | rate TOP/s | % of peak |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    digests = set()
+    for d, js in runs:
+        out = _bench_line(js)
+        digests.add(out["kernel_digest"])
+        rows = _rows(d, "counter_collection.csv")
+        util = _counter(rows, "MfmaUtil")
+        mops = _counter(rows, "SQ_INSTS_VALU_MFMA_MOPS_I8")
+        inst = _counter(rows, "SQ_INSTS_VALU_MFMA_I8")
+        rf = out["roofline"]
+        launch_us = rf["mean_launch_us"]
+        alg = rf["mean_algorithmic_int8_ops_per_launch"]
+        by = {}
+        for did, (k, v) in util.items():
+            n = _short(k)
+            if not _is_linear(n):
+                continue
+            b = by.setdefault(_policy(n), [[], [], []])
+            b[0].append(v)
+            b[1].append(mops.get(did, (k, 0.0))[1] * 512.0)
+            b[2].append(inst.get(did, (k, 0.0))[1])
+        cfg = out["config"]
+        for pol, (u, o, ni) in sorted(by.items()):
+            ex = statistics.mean(o)
+            rate = ex / (launch_us * 1e-6) / 1e12
+            lines.append(f"| {cfg['workload']} | {cfg['M']} | `{pol}` | {len(u)} | {statistics.mean(u):.2f} | "
+                         f"{statistics.mean(ni):.0f} | {ex / 1e9:.3f} | {alg / 1e9:.3f} | {ex / alg:.2f} | "
+                         f"{launch_us:.2f} | {rate:.1f} | {100 * rate / PEAK_I8_TOPS:.2f} |")
+    lines += ["", "digest: " + ", ".join(sorted(digests)), ""]
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="summarize rocprofv3 runs of bench.py")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -185,6 +251,10 @@ def main(argv=None):
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--only", default=None, help="keep the kernels whose name starts with this")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("runs", nargs="+", help="<counter dir>=<bench.py output of a plain run, same workload and M>")
+    mf.add_argument("--cmd", required=True)
+    mf.add_argument("--out", required=True)
     c = sub.add_parser("traffic")
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
@@ -198,6 +268,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.what == "trace":
         text = trace_summary(a.dir, a.cmd, a.only)
+    elif a.what == "mfma":
+        text = mfma_summary([tuple(r.split("=", 1)) for r in a.runs], a.cmd)
     else:
         text = traffic_summary(a.fetch_dir, a.write_dir, a.calib_mib, a.workload, a.m, a.cmd,
                                a.fetch_json, a.write_json)
