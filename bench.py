@@ -16,7 +16,8 @@ Printed: ONE JSON line.  `value` is algorithmic bytes per pass (packed weights,
 scales and zeros, int8 activations in, fp32 outputs out) / wall time per pass,
 in GB/s.  `roofline` reports the dominant kernel (the linear) timed per launch
 with HIP events on its stream; `cpu_baseline` times the CPU oracle on one
-layer of the same workload.
+layer of the same workload; `hbm_stream_reference` is a plain device copy's
+rate on the same GPU, measured beside the 8 TB/s peak the fractions use.
 
 The pages behind the method ("Karpathy's Trick for Faster Local LLMs Finally
 Has Proper Tooling", blog.dailydoseofds.com, section "Why batch-one decoding
@@ -288,6 +289,40 @@ def profiled_traffic(workload, M):
     return float(val.group(1)), os.path.relpath(path, ROOT)
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu's), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def copy_stream_reference(torch, dev, mib=1024, reps=5):
+    """A plain device-to-device copy (torch) of `mib` MiB, as a measured
+    streaming rate of this GPU beside the 8 TB/s peak: (read + write bytes) /
+    time, the best of `reps` copies timed with events."""
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return {"kind": f"torch device-to-device copy of {mib} MiB, (read + write bytes) / time, best of {reps}",
+            "GB_per_s": round(2 * (mib << 20) / (best * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(stack, M, min_seconds=12.0, max_reps=32):
     """The CPU oracle on a bounded sample of the same workload: the four
     launches of layer 0 (weights copied from the device generator and encoded
@@ -327,7 +362,7 @@ def cpu_baseline(stack, M, min_seconds=12.0, max_reps=32):
                        f"algorithmic bytes each time) on the activations of {reps} layers at M={M}: "
                        f"activation RHT + int8 quantization, exact integer contraction, fp64 output; "
                        f"numpy, one thread; {dt:.1f} s timed",
-                seconds=dt, cpu=platform.processor() or platform.machine())
+                seconds=dt, cpu=cpu_model(), cores_available=len(os.sched_getaffinity(0)))
 
 
 def time_tree_accept(torch, dev, T, V, reps=50):
@@ -516,7 +551,9 @@ def main():
                    "fused_activation_quantization": one},
         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "passes_per_s": round(1e3 / ms, 2),
-        "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1)},
+        "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1),
+                                 # the pages' measured tokens per verify pass on their machine: context only
+                                 "tau_8.39_pages_context": round(8.39 * 1e3 / ms, 1)},
         "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M, stack.fused),
                      "achieved": round(k_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
@@ -571,6 +608,9 @@ def main():
         print(f"[bench] delta-rule tree T={dn['T']} H={dn['H']}: verify {dn['verify_us']:.2f} us, "
               f"commit {dn['commit_us']:.2f} us", file=sys.stderr, flush=True)
         out["tree_deltanet"] = dn
+    out["hbm_stream_reference"] = copy_stream_reference(torch, dev)
+    print(f"[bench] reference copy stream: {out['hbm_stream_reference']['GB_per_s']} GB/s", file=sys.stderr,
+          flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
         cb = cpu_baseline(stack, M)
