@@ -312,8 +312,12 @@ def test_fused_in_captured_graph():
 
 
 # ------------------------------------------------- full-size stack launches
-STACK_CASES = [("stack_w4g64", 16, "qkv"), ("stack_w4g64", 16, "down"), ("stack_w4g64", 1, "gateup"),
-               ("stack_w4g64", 1, "down"), ("stack_w8", 32, "qkv"), ("stack_w8", 32, "down"),
+# every launch kind of the timed passes (W4 g64 at M = 16 and 1, W8 at M = 32),
+# and the g128 sweep's M values
+STACK_CASES = [("stack_w4g64", 16, "qkv"), ("stack_w4g64", 16, "o"), ("stack_w4g64", 16, "gateup"),
+               ("stack_w4g64", 16, "down"), ("stack_w4g64", 1, "qkv"), ("stack_w4g64", 1, "o"),
+               ("stack_w4g64", 1, "gateup"), ("stack_w4g64", 1, "down"), ("stack_w8", 32, "qkv"),
+               ("stack_w8", 32, "o"), ("stack_w8", 32, "gateup"), ("stack_w8", 32, "down"),
                ("stack_w8", 1, "o"), ("stack_w4g128", 32, "down"), ("stack_w4g128", 32, "gateup"),
                ("stack_w4g128", 1, "qkv"), ("stack_w4g128", 2, "gateup"), ("stack_w4g128", 4, "down"),
                ("stack_w4g128", 8, "o"), ("stack_w4g128", 16, "qkv")]
