@@ -174,6 +174,50 @@ def test_full_size_single_matrix(src):
     check_y(C.host(y), y_ref)
 
 
+# ------------------------------------------------------------ maximum sizes
+def test_w8_partials_reach_the_int32_bound():
+    """W8 at its largest K (131072) and M (32), on inputs with one non-zero
+    value per 32-block (the first): the rotated block is that value times its
+    sign in all 32 places (the first Hadamard column is all ones), so every
+    activation and weight code is +-127 with the same sign on both sides and
+    S = 127^2 * K = 2,114,060,288 in every output -- just under 2^31, which
+    the int32 accumulation must reach without wrapping."""
+    M, N, K = 32, 16, 131072
+    _x, _W, signs = synth.random_case(1, 1, K, seed=131072)
+    x = np.zeros((M, K), np.float32)
+    x[:, ::32] = (1.0 + np.arange(M, dtype=np.float32) / 64.0)[:, None]
+    W = np.zeros((N, K), np.float32)
+    W[:, ::32] = (0.02 * (1.0 + np.arange(N, dtype=np.float32) / 8.0))[:, None]
+    C.say(f"w8 int32 bound M={M} N={N} K={K}")
+    ow = O.prepare_w8(W, signs)
+    y_ref, S_ref, qx, sx = O.linear_w8(x, signs, ow)
+    assert (np.abs(qx) == 127).all() and (np.abs(ow["q"]) == 127).all()
+    assert (S_ref == 127 * 127 * K).all()
+    w = C.gpu_prepare(W, signs, "w8", 0)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert (C.host(dbg).astype(np.int64) == 127 * 127 * K).all()
+    check_y(C.host(y), y_ref)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_w4_long_k(M):
+    """K = 2^20: the linear's plain loop (no resident launch shape holds that
+    many chunks per wave) and the stand-alone activation kernel reading each
+    row twice, at a length far beyond the workloads'."""
+    N, K, g = 16, 1 << 20, 64
+    x, W, signs = synth.random_case(M, N, K, seed=M + 20)
+    C.say(f"w4 long K M={M} N={N} K={K}")
+    ow = O.prepare_w4(W, signs, g)
+    y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
+    w = C.gpu_prepare(W, signs, "w4_z16", g)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+    assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
+    check_y(C.host(y), y_ref)
+
+
 def test_rejects_bad_arguments_without_writing():
     import speculative_verify_gemm_amd as svg
     xq = torch.zeros((2, 64), dtype=torch.int8, device=C.DEV)
