@@ -218,6 +218,71 @@ def test_w4_long_k(M):
     check_y(C.host(y), y_ref)
 
 
+# ------------------------------------------------------- extreme magnitudes
+def _scaled_rows(a, scales):
+    """Rows of `a` rescaled to the given maximum magnitudes (0 gives zeros)."""
+    peak = np.abs(a).max(axis=1, keepdims=True)
+    return (a / peak * np.asarray(scales, np.float32)[:, None]).astype(np.float32)
+
+
+def test_act_codes_extreme_rows():
+    """Rows whose maxima span fp32: a denormal row (its scale sigma * 2^-5
+    underflows to 0 and 1 / sigma overflows, so every code takes the exact
+    division), the edge of the normal range, and rows up to 1e36 (the
+    transform's sums of 32 stay finite).  Codes and scales bit-exact."""
+    M, K = 6, 1024
+    x, _W, signs = synth.random_case(M, 1, K, seed=77, x_kind="student_t3")
+    x = _scaled_rows(x, [1e-42, 1e-39, 1e-30, 1.0, 1e30, 1e36])
+    qx, sx = O.quant_acts(x, signs)
+    xq, xs = C.gpu_quant_acts(x, signs)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,group", [("w4_z4", 32), ("w4_z16", 64), ("w4_z16", 128), ("w8", 0)])
+def test_weight_codes_extreme_rows(fmt, group):
+    """Weight rows from zero through scales below fp16's range (the scale
+    falls back to 1.0) and in its subnormal range, up to 1e3.  Codes,
+    scales and zeros bit-exact."""
+    N, K = 21, 384
+    _x, W, signs = synth.random_case(1, N, K, seed=78)
+    W = np.nan_to_num(_scaled_rows(W, np.repeat([0.0, 1e-30, 1e-7, 3e-5, 1e-3, 1.0, 1e3], 3)))
+    w = C.gpu_prepare(W, signs, fmt, group)
+    u = O.rht(W, signs)
+    if fmt == "w8":
+        q, s = O.quant_w8(u)
+        ow = dict(q=q, s=s)
+    else:
+        q, s, z = O.quant_w4(u, group)
+        ow = dict(q=q, s=s, z=z, group=group)
+    wq, ws, wz = C.oracle_storage(ow, fmt, K)
+    assert np.array_equal(C.host(w["wq"]).view(np.uint8), wq.view(np.uint8).reshape(-1))
+    assert np.array_equal(C.host(w["ws"]).view(np.uint16), ws.view(np.uint16).reshape(-1))
+    if wz is not None:
+        assert np.array_equal(C.host(w["wz"]).view(np.uint8), wz.view(np.uint8).reshape(-1))
+
+
+@pytest.mark.parametrize("fmt,group,M", [("w4_z16", 64, 1), ("w4_z16", 64, 16), ("w8", 0, 32)])
+def test_linear_extreme_rows(fmt, group, M):
+    """The whole call on rows of very different magnitudes (activations from
+    1e-20 to 1e20, weights from fp16-subnormal scales to 1e3), with every
+    output inside fp32's normal range: partial sums bit-exact, y within
+    tolerance row by row."""
+    N, K = 35, 512
+    x, W, signs = synth.random_case(M, N, K, seed=79 + M)
+    x = _scaled_rows(x, np.resize([1e-20, 1e-5, 1.0, 1e10, 1e20], M))
+    W = _scaled_rows(W, np.resize([3e-5, 1e-3, 1.0, 1e3, 0.02], N))
+    if fmt == "w8":
+        y_ref, S_ref, qx, sx = O.linear_w8(x, signs, O.prepare_w8(W, signs))
+    else:
+        y_ref, S_ref, qx, sx = O.linear_w4(x, signs, O.prepare_w4(W, signs, group))
+    w = C.gpu_prepare(W, signs, fmt, group)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
+    check_y(C.host(y), y_ref)
+
+
 def test_rejects_bad_arguments_without_writing():
     import speculative_verify_gemm_amd as svg
     xq = torch.zeros((2, 64), dtype=torch.int8, device=C.DEV)
