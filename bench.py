@@ -608,9 +608,10 @@ def main():
         print(f"[bench] delta-rule tree T={dn['T']} H={dn['H']}: verify {dn['verify_us']:.2f} us, "
               f"commit {dn['commit_us']:.2f} us", file=sys.stderr, flush=True)
         out["tree_deltanet"] = dn
-    out["hbm_stream_reference"] = copy_stream_reference(torch, dev)
-    print(f"[bench] reference copy stream: {out['hbm_stream_reference']['GB_per_s']} GB/s", file=sys.stderr,
-          flush=True)
+    if not args.calib_copy_mib:  # counter runs calibrate on their own copy and time nothing
+        out["hbm_stream_reference"] = copy_stream_reference(torch, dev)
+        print(f"[bench] reference copy stream: {out['hbm_stream_reference']['GB_per_s']} GB/s", file=sys.stderr,
+              flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
         cb = cpu_baseline(stack, M)

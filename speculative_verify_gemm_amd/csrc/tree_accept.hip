@@ -42,9 +42,11 @@ constexpr int kUnroll = 8;  // float4 loads in flight per thread
 typedef unsigned long long u64;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Monotone map of fp32 to u32 (larger value -> larger code; -0 < +0).
+// Monotone map of fp32 to u32 (larger value -> larger code).  -0 and +0 are
+// one value (equal maxima go to the smaller index), so -0 takes +0's code:
+// -0 + 0 = +0 when rounding to nearest.
 SVG_DEV u32 order_bits(float v) {
-  const u32 b = __float_as_uint(v);
+  const u32 b = __float_as_uint(v + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 SVG_DEV u64 make_key(float v, u32 idx) { return ((u64)order_bits(v) << 32) | (u64)(0xFFFFFFFFu - idx); }

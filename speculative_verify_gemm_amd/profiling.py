@@ -141,8 +141,10 @@ def _counter(rows, counter):
 
 def _scale(vals, calib_kib):
     """Factor that maps the counter onto true KiB, from the calibration copy:
-    the copy dispatches reading at least half of its size."""
-    copies = [v for k, v in vals.values() if COPY_KERNEL in k and v >= 0.5 * calib_kib]
+    the copy dispatches whose reading lies between a quarter and 1.5 times
+    its size (FETCH_SIZE reads half of it, WRITE_SIZE all of it; copies of
+    other sizes in the same run fall outside)."""
+    copies = [v for k, v in vals.values() if COPY_KERNEL in k and 0.25 * calib_kib <= v <= 1.5 * calib_kib]
     if not copies:
         raise SystemExit("no calibration copy found in the counter run")
     return calib_kib / statistics.median(copies), len(copies)

@@ -90,6 +90,32 @@ def test_accept_then_commit(T, H, dk, dv):
     close(C.host(Sd), ref)
 
 
+@pytest.mark.parametrize("T,H,dk,dv", [(16, 4, 128, 128), (9, 3, 64, 256)])
+def test_gates_at_their_bounds(T, H, dk, dv):
+    """Decay and write strength at the ends of their ranges, mixed over the
+    tree: alpha = 1 (no decay), beta = 0 (no write: only the decay acts),
+    beta = 1 (the key's old value replaced), and alpha near 0."""
+    S0, q, k, v, a, b, parent = synth.deltanet_case(T, H, dk, dv, seed=31 + T, shape="bushy")
+    a = a.copy()
+    b = b.copy()
+    a[::3] = 1.0
+    a[1::5] = 1e-3
+    b[::4] = 0.0
+    b[2::4] = 1.0
+    case = (S0, q, k, v, a, b, parent)
+    Sd, qd, kd, vd, ad, bd, pd = dev(case)
+    out = torch.empty((T, H, dv), dtype=torch.float32, device=C.DEV)
+    svg.tree_deltanet_verify(Sd, qd, kd, vd, ad, bd, pd, out)
+    close(C.host(out), DN.tree_verify(*case))
+    path = TO.root_path(parent, T - 1)[1:]
+    n = torch.tensor([len(path) + 1], dtype=torch.int32, device=C.DEV)
+    pathd = torch.full((T,), -1, dtype=torch.int32, device=C.DEV)
+    if path:
+        pathd[:len(path)] = C.to_dev(np.array(path, np.int32))
+    svg.tree_deltanet_commit(Sd, kd, vd, ad, bd, pathd, n)
+    close(C.host(Sd), DN.tree_commit(*case, path))
+
+
 def test_commit_of_a_rejected_tree_leaves_the_state():
     T, H, dk, dv = 6, 2, 128, 128
     case = synth.deltanet_case(T, H, dk, dv, seed=11)

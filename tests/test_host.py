@@ -84,8 +84,10 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     calib_kib = 256 * 1024
     # FETCH_SIZE reads half of the copy (scale 2), WRITE_SIZE all of it (scale 1)
     fetch = [[i, COPY, "FETCH_SIZE", calib_kib / 2] for i in range(3)]
+    fetch += [[5, COPY, "FETCH_SIZE", calib_kib * 2]]  # a 1 GiB copy of the same run: not the calibration
     fetch += [[10, LIN.format("8, 4, 4"), "FETCH_SIZE", 1000.0], [11, LIN.format("8, 4, 4"), "FETCH_SIZE", 3000.0]]
     write = [[i, COPY, "WRITE_SIZE", calib_kib] for i in range(3)]
+    write += [[5, COPY, "WRITE_SIZE", calib_kib * 4]]
     write += [[10, LIN.format("8, 4, 4"), "WRITE_SIZE", 10.0], [11, LIN.format("8, 4, 4"), "WRITE_SIZE", 30.0]]
     _csv(str(tmp_path / "f" / "pmc_counter_collection.csv"), hdr, fetch)
     _csv(str(tmp_path / "w" / "pmc_counter_collection.csv"), hdr, write)

@@ -142,8 +142,10 @@ def test_target_choice_is_the_first_maximum():
     logits = np.array([[0, 3, 1, 3, 2],
                        [4, 4, 4, 4, 4],
                        [-np.inf, -np.inf, -1, -np.inf, -1],
-                       [1, 2, 3, 4, 5]], dtype=np.float32)
-    assert list(TO.target_choices(logits)) == [1, 0, 2, 4]
+                       [1, 2, 3, 4, 5],
+                       [-1, -0.0, -2, 0.0, -3],     # -0 and +0 are one value
+                       [-1, 0.0, -2, -0.0, -3]], dtype=np.float32)
+    assert list(TO.target_choices(logits)) == [1, 0, 2, 4, 1, 1]
     with pytest.raises(ValueError):
         TO.target_choices(np.zeros((2, 0), np.float32))
 

@@ -95,6 +95,26 @@ def test_unaligned_rows_take_the_elementwise_loads():
     check(gpu_tree(view, parent, draft, svg.tree_workspace()), logits, parent, draft)
 
 
+def test_infinite_logits():
+    """Rows holding +inf (the first +inf wins), rows entirely -inf (index 0
+    wins), -0.0 against +0.0 (equal values: the first wins, whichever sign it
+    has) and the largest finite values: the order on the keys is the order of
+    the floats."""
+    T, V = 12, 3000
+    logits, parent, draft = synth.draft_tree(T, V, seed=21, accept=5, ties=True)
+    logits = logits.copy()
+    logits[1, [7, 2900]] = np.inf
+    logits[2, :] = -np.inf
+    logits[3, :] = 0.0
+    logits[3, 5] = -0.0
+    logits[3, 4] = -0.0
+    logits[4, [10, 11]] = np.finfo(np.float32).max
+    logits[5, 0] = -np.inf
+    logits[6, :] = -1.0
+    logits[6, [3, 9]] = [-0.0, 0.0]  # equal maxima: -0.0 comes first and wins
+    check(gpu_tree(C.to_dev(logits), parent, draft, svg.tree_workspace()), logits, parent, draft)
+
+
 def test_malformed_tree_is_flagged():
     T, V = 6, 50
     logits, parent, draft = synth.draft_tree(T, V, seed=4, accept=3)
