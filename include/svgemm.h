@@ -261,8 +261,8 @@ svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* sig
  *  One launch: the logits stream once (T * V * 4 bytes); the workgroup that
  *  finishes last reads the row maxima and walks the tree.
  *  Errors: SVG_EINVAL for a null pointer, T < 1 or V < 1; SVG_EUNSUPPORTED for
- *  T > SVG_TREE_MAX_NODES or V > 2^30; SVG_EALIGN for logits not 4-byte or
- *  workspace not 8-byte aligned.
+ *  T > SVG_TREE_MAX_NODES or V > 2^30; SVG_EALIGN for logits, parent, draft
+ *  or an output not 4-byte aligned, or workspace not 8-byte aligned.
  */
 enum { SVG_TREE_MAX_NODES = 32, SVG_TREE_WORKSPACE_BYTES = 512 };
 svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* parent,

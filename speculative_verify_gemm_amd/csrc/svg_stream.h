@@ -32,6 +32,7 @@
 //   p.finish(t, slot)                reduce through LDS buffer `slot`, store, reset
 #pragma once
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "svg_act.h"
@@ -263,13 +264,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
 // its occupancy is fixed when it is built).
 template <auto KERNEL>
 int resident_blocks(int block) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int v = 0;
+  static std::atomic<int> per_cu{0};  // every calling thread finds the same value
+  int v = per_cu.load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, KERNEL, block, 0) != hipSuccess || v < 1) v = 1;
-    per_cu = v;
+    per_cu.store(v, std::memory_order_relaxed);
   }
-  return per_cu * svg_cu_count();
+  return v * svg_cu_count();
 }
 
 // Persistent grid: at most as many workgroups as fit at once, and the tiles

@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include <atomic>
 #include <cstdio>
 #include <string>
 
@@ -60,15 +61,15 @@ bool fits_w8(int N, int K) {
 }  // namespace
 
 int svg_cu_count() {
-  static int counts[64] = {0};
+  static std::atomic<int> counts[64];  // per device; every calling thread finds the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (counts[dev] == 0) {
-    int c = 0;
+  int c = counts[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 1;
-    counts[dev] = c;
+    counts[dev].store(c, std::memory_order_relaxed);
   }
-  return counts[dev];
+  return c;
 }
 
 extern "C" {
@@ -264,7 +265,9 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
   if (T < 1 || V < 1) return fail(SVG_EINVAL, fn, "T and V must be >= 1");
   if (T > SVG_TREE_MAX_NODES) return fail(SVG_EUNSUPPORTED, fn, "T > SVG_TREE_MAX_NODES");
   if (V > kMaxV) return fail(SVG_EUNSUPPORTED, fn, "V > 2^30");
-  if (!aligned(logits, 4)) return fail(SVG_EALIGN, fn, "logits must be 4-byte aligned");
+  if (!aligned(logits, 4) || !aligned(parent, 4) || !aligned(draft, 4) || !aligned(target, 4) || !aligned(path, 4) ||
+      !aligned(emit, 4) || !aligned(n_emit, 4))
+    return fail(SVG_EALIGN, fn, "logits, parent, draft and the outputs must be 4-byte aligned");
   if (!aligned(workspace, 8)) return fail(SVG_EALIGN, fn, "workspace must be 8-byte aligned");
   return hip_status(fn, svg_launch_tree_accept(logits, T, V, parent, draft, target, path, emit, n_emit, workspace,
                                                reinterpret_cast<hipStream_t>(stream)));

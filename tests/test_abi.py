@@ -193,7 +193,8 @@ def _tree(svg, **kw):
     (dict(path=NULL), 1), (dict(emit=NULL), 1), (dict(n=NULL), 1), (dict(ws=NULL), 1),
     (dict(T=0), 1), (dict(V=0), 1), (dict(T=-2), 1),
     (dict(T=33), 2),
-    (dict(logits=MIS), 3), (dict(ws=ctypes.c_void_p(0x10004)), 3),
+    (dict(logits=MIS), 3), (dict(ws=ctypes.c_void_p(0x10004)), 3), (dict(parent=MIS), 3),
+    (dict(draft=MIS), 3), (dict(target=MIS), 3), (dict(path=MIS), 3), (dict(emit=MIS), 3), (dict(n=MIS), 3),
 ])
 def test_tree_accept_validation(svg, kw, code):
     assert _tree(svg, **kw) == code
