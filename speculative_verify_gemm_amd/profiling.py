@@ -206,7 +206,9 @@ def mfma_summary(runs, cmd):
     lines = ["# rocprofv3 MFMA counters of the linear kernels", "", "Commands (one counter run per row group):", "",
              "```", cmd, "```", "",
              "Per linear kernel of each run: `busy` = MfmaUtil, the matrix unit's busy cycles over all SIMDs "
-             "divided by (GPU-active cycles x SIMDs) during the dispatch, so launch ramp and tail count as idle; "
+             "divided by (GPU-active cycles x SIMDs) during the dispatch, so launch ramp and tail count as idle "
+             "(and the counter run serializes dispatches, which lengthens each one's active window: `busy` reads "
+             "lower than `% of peak`, which divides by the plain run's launch time); "
              "`executed` = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512 int8 operations per launch; `algorithmic` = "
              "2*M*N*K per launch (the MFMA form executes more: rows padded to 16 tokens, the zero-point "
              "MFMA of W4); `rate` = executed operations over the mean linear launch duration of a plain "
