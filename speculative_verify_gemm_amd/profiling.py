@@ -207,8 +207,9 @@ def mfma_summary(runs, cmd):
              "```", cmd, "```", "",
              "Per linear kernel of each run: `busy` = MfmaUtil, the matrix unit's busy cycles over all SIMDs "
              "divided by (GPU-active cycles x SIMDs) during the dispatch, so launch ramp and tail count as idle "
-             "(and the counter run serializes dispatches, which lengthens each one's active window: `busy` reads "
-             "lower than `% of peak`, which divides by the plain run's launch time); "
+             "(it reads about half of `% of peak`: the two use different time bases -- the serialized dispatches "
+             "of the counter run against the plain run's launch time -- and the busy cycles the counter charges "
+             "per MFMA instruction are not documented; `% of peak` is the figure quoted); "
              "`executed` = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512 int8 operations per launch; `algorithmic` = "
              "2*M*N*K per launch (the MFMA form executes more: rows padded to 16 tokens, the zero-point "
              "MFMA of W4); `rate` = executed operations over the mean linear launch duration of a plain "
