@@ -84,6 +84,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CALIB_SRC = os.path.join(HERE, "calib", "mfma_peak.hip")
+CALIB_BIN = os.path.join(HERE, "calib", "mfma_peak")
+
+
+def build_calibration(verbose: bool = False) -> str:
+    """The int8 MFMA calibration program (not part of the library)."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", CALIB_SRC, "-o", CALIB_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {CALIB_BIN}")
+    return CALIB_BIN
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_calibration(verbose=True)
     sys.exit(0)

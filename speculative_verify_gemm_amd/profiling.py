@@ -2,6 +2,7 @@
 
     python -m speculative_verify_gemm_amd.profiling trace <trace dir> --cmd "<command>" --out <file.md>
     python -m speculative_verify_gemm_amd.profiling mfma <pmc dir>=<bench out> ... --cmd "<commands>" --out <file.md>
+    python -m speculative_verify_gemm_amd.profiling calib <program output> <counter dir> <MfmaUtil dir> --cmd ... --out ...
     python -m speculative_verify_gemm_amd.profiling traffic <fetch dir> <write dir> --calib-mib 256 \\
         --workload stack_w4g64 --m 16 --fetch-json <bench out> --write-json <bench out> \\
         --cmd "<commands>" --out <file.md>
@@ -17,6 +18,10 @@ collection serializes the dispatches) of the same workload and M, and lists
 per linear kernel the share of SIMD cycles the matrix unit was busy, the int8
 operations it executed per launch against the algorithmic 2*M*N*K, and the
 executed rate over the plain run's mean launch duration.
+
+`calib` summarizes the int8 MFMA calibration program (calib/mfma_peak.hip):
+its throughput, and the busy cycles and operations the counters charge per
+MFMA instruction.
 
 `traffic` reads two counter runs (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`):
 each counter is scaled by what it reads for the device-to-device copy of
@@ -207,9 +212,9 @@ def mfma_summary(runs, cmd):
              "```", cmd, "```", "",
              "Per linear kernel of each run: `busy` = MfmaUtil, the matrix unit's busy cycles over all SIMDs "
              "divided by (GPU-active cycles x SIMDs) during the dispatch, so launch ramp and tail count as idle "
-             "(it reads about half of `% of peak`: the two use different time bases -- the serialized dispatches "
-             "of the counter run against the plain run's launch time -- and the busy cycles the counter charges "
-             "per MFMA instruction are not documented; `% of peak` is the figure quoted); "
+             "(the counter charges 16 busy cycles per v_mfma_i32_16x16x64_i8, profiles/mfma_i8_calibration.md, "
+             "so `busy` reading about half of `% of peak` is the time base: a serialized dispatch of the counter "
+             "run stays active about twice as long as the plain run's launch; `% of peak` is the figure quoted); "
              "`executed` = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512 int8 operations per launch; `algorithmic` = "
              "2*M*N*K per launch (the MFMA form executes more: rows padded to 16 tokens, the zero-point "
              "MFMA of W4); `rate` = executed operations over the mean linear launch duration of a plain "
@@ -248,6 +253,39 @@ def mfma_summary(runs, cmd):
     return "\n".join(lines)
 
 
+def calib_summary(plain_txt, counter_dir, util_dir, cmd):
+    """The int8 MFMA calibration program (calib/mfma_peak.hip): its printed
+    throughput per occupancy, and per timed dispatch the busy cycles and int8
+    operations the counters charge per MFMA instruction."""
+    with open(plain_txt) as f:
+        printed = [ln.strip() for ln in f if ln.startswith("waves per SIMD")]
+    rows = _rows(counter_dir, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        d = by.setdefault(r["Dispatch_Id"], {"kernel": _short(r["Kernel_Name"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    util = {did: v for did, (_k, v) in _counter(_rows(util_dir, "counter_collection.csv"), "MfmaUtil").items()}
+    lines = ["# Calibration of the int8 MFMA pipe (v_mfma_i32_16x16x64_i8)", "", "Commands:", "", "```", cmd, "```",
+             "", "Throughput (plain run, HIP events; 256 workgroups, four independent accumulator chains per "
+             "wave):", ""]
+    lines += [f"- {ln}" for ln in printed]
+    lines += ["", "Counters of the timed dispatches (the larger of each kernel's two):", "",
+              "| kernel | MFMA instructions | busy cycles / instruction | int8 ops / instruction | MfmaUtil % |",
+              "|---|---|---|---|---|"]
+    best = {}
+    for did, d in by.items():
+        n = d.get("SQ_INSTS_VALU_MFMA_I8", 0.0)
+        if n and n > best.get(d["kernel"], (0, None))[0]:
+            best[d["kernel"]] = (n, did)
+    for k, (n, did) in sorted(best.items()):
+        d = by[did]
+        u = util.get(did)
+        lines.append(f"| `{k}` | {n:.0f} | {d['SQ_VALU_MFMA_BUSY_CYCLES'] / n:.2f} | "
+                     f"{d['SQ_INSTS_VALU_MFMA_MOPS_I8'] * 512 / n:.0f} | {'' if u is None else f'{u:.1f}'} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="summarize rocprofv3 runs of bench.py")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -260,6 +298,12 @@ def main(argv=None):
     mf.add_argument("runs", nargs="+", help="<counter dir>=<bench.py output of a plain run, same workload and M>")
     mf.add_argument("--cmd", required=True)
     mf.add_argument("--out", required=True)
+    cb = sub.add_parser("calib")
+    cb.add_argument("plain", help="output of calib/mfma_peak")
+    cb.add_argument("counter_dir", help="--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_I8 SQ_INSTS_VALU_MFMA_MOPS_I8")
+    cb.add_argument("util_dir", help="--pmc MfmaUtil")
+    cb.add_argument("--cmd", required=True)
+    cb.add_argument("--out", required=True)
     c = sub.add_parser("traffic")
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
@@ -273,6 +317,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.what == "trace":
         text = trace_summary(a.dir, a.cmd, a.only)
+    elif a.what == "calib":
+        text = calib_summary(a.plain, a.counter_dir, a.util_dir, a.cmd)
     elif a.what == "mfma":
         text = mfma_summary([tuple(r.split("=", 1)) for r in a.runs], a.cmd)
     else:

@@ -128,3 +128,18 @@ def test_mfma_summary_arithmetic(tmp_path):
     assert cells[8] == "2.00"                         # executed / algorithmic
     assert cells[10] == "1.3" and cells[11] == "0.03"  # 1.28 TOP/s, 0.0256 % of 5000
     assert "digest: abc" in text
+
+
+def test_calib_summary_per_instruction(tmp_path):
+    (tmp_path / "plain.txt").write_text("waves per SIMD 4: 2.5 ms, 100 MFMA, 4289.8 TOP/s int8, 18.77 cycles\n")
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "void k_mfma_peak<16>(int*, int)"
+    rows = [[1, k, "SQ_INSTS_VALU_MFMA_I8", 10.0], [1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 160.0],
+            [1, k, "SQ_INSTS_VALU_MFMA_MOPS_I8", 640.0],                       # warm-up dispatch
+            [2, k, "SQ_INSTS_VALU_MFMA_I8", 1000.0], [2, k, "SQ_VALU_MFMA_BUSY_CYCLES", 16000.0],
+            [2, k, "SQ_INSTS_VALU_MFMA_MOPS_I8", 64000.0]]                     # timed: 64 x 512 ops each
+    _csv(str(tmp_path / "c" / "pmc_counter_collection.csv"), hdr, rows)
+    _csv(str(tmp_path / "u" / "pmc_counter_collection.csv"), hdr, [[1, k, "MfmaUtil", 5.0], [2, k, "MfmaUtil", 91.9]])
+    text = P.calib_summary(str(tmp_path / "plain.txt"), str(tmp_path / "c"), str(tmp_path / "u"), "cmd")
+    assert "- waves per SIMD 4: 2.5 ms" in text
+    assert "| `k_mfma_peak<16>` | 1000 | 16.00 | 32768 | 91.9 |" in text
