@@ -84,20 +84,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-CALIB_SRC = os.path.join(HERE, "calib", "mfma_peak.hip")
-CALIB_BIN = os.path.join(HERE, "calib", "mfma_peak")
+CALIB = os.path.join(HERE, "calib")
+CALIB_PROGRAMS = ("mfma_peak", "hbm_read")
 
 
-def build_calibration(verbose: bool = False) -> str:
-    """The int8 MFMA calibration program (not part of the library)."""
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", CALIB_SRC, "-o", CALIB_BIN]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    if verbose:
-        print(f"built {CALIB_BIN}")
-    return CALIB_BIN
+def build_calibration(verbose: bool = False) -> list:
+    """The calibration programs (not part of the library): the int8 MFMA pipe
+    and HBM streaming, measured on the GPU they run on."""
+    out = []
+    for name in CALIB_PROGRAMS:
+        exe = os.path.join(CALIB, name)
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", os.path.join(CALIB, name + ".hip"), "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        if verbose:
+            print(f"built {exe}")
+        out.append(exe)
+    return out
 
 
 if __name__ == "__main__":

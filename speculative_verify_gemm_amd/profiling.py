@@ -23,6 +23,9 @@ executed rate over the plain run's mean launch duration.
 its throughput, and the busy cycles and operations the counters charge per
 MFMA instruction.
 
+`hbm` summarizes the HBM read calibration program (calib/hbm_read.hip): per
+size, the time per launch and the dispatch spans of a kernel trace.
+
 `traffic` reads two counter runs (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`):
 each counter is scaled by what it reads for the device-to-device copy of
 `--calib-mib` MiB that bench.py makes first (`--calib-copy-mib`), whose true
@@ -286,6 +289,37 @@ def calib_summary(plain_txt, counter_dir, util_dir, cmd):
     return "\n".join(lines)
 
 
+def hbm_summary(plain_txt, trace_dir, cmd, reps=50):
+    """The HBM read calibration program (calib/hbm_read.hip): its printed
+    per-launch times (events around back-to-back launches) and, from a kernel
+    trace of the same program, the dispatch spans of the timed launches of
+    each size (the program launches three untimed, then the timed ones, size
+    after size)."""
+    import re
+    with open(plain_txt) as f:
+        printed = [ln.rstrip() for ln in f if ln.startswith("read ")]
+    spans = []
+    for r in sorted(_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        if _short(r["Kernel_Name"]).startswith("k_read"):
+            spans.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# HBM read calibration (read-only streaming kernel)", "", "Commands:", "", "```", cmd, "```", "",
+             "| size | bytes | us per launch (events, back to back) | GB/s | median dispatch span us (trace) | "
+             "GB/s over the span |", "|---|---|---|---|---|---|"]
+    pos = 0
+    for ln in printed:
+        m = re.match(r"read (.+?)\s+(\d+) bytes:\s+([\d.]+) us per launch,\s+([\d.]+) GB/s", ln)
+        if not m:
+            continue
+        what, nbytes, us, gbps = m.group(1), int(m.group(2)), float(m.group(3)), float(m.group(4))
+        n = 5 if nbytes >= (1 << 30) else reps  # the program times 5 launches of the GiB sizes
+        timed = spans[pos + 3: pos + 3 + n]
+        pos += 3 + n
+        med = statistics.median(timed) if timed else float("nan")
+        lines.append(f"| {what} | {nbytes} | {us:.2f} | {gbps:.1f} | {med:.2f} | {nbytes / (med * 1e-6) / 1e9:.1f} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="summarize rocprofv3 runs of bench.py")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -304,6 +338,12 @@ def main(argv=None):
     cb.add_argument("util_dir", help="--pmc MfmaUtil")
     cb.add_argument("--cmd", required=True)
     cb.add_argument("--out", required=True)
+    hb = sub.add_parser("hbm")
+    hb.add_argument("plain", help="output of calib/hbm_read")
+    hb.add_argument("trace_dir", help="--kernel-trace of the same program")
+    hb.add_argument("--reps", type=int, default=50, help="the launches per size the program was given")
+    hb.add_argument("--cmd", required=True)
+    hb.add_argument("--out", required=True)
     c = sub.add_parser("traffic")
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
@@ -317,6 +357,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.what == "trace":
         text = trace_summary(a.dir, a.cmd, a.only)
+    elif a.what == "hbm":
+        text = hbm_summary(a.plain, a.trace_dir, a.cmd, a.reps)
     elif a.what == "calib":
         text = calib_summary(a.plain, a.counter_dir, a.util_dir, a.cmd)
     elif a.what == "mfma":

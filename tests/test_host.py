@@ -143,3 +143,21 @@ def test_calib_summary_per_instruction(tmp_path):
     text = P.calib_summary(str(tmp_path / "plain.txt"), str(tmp_path / "c"), str(tmp_path / "u"), "cmd")
     assert "- waves per SIMD 4: 2.5 ms" in text
     assert "| `k_mfma_peak<16>` | 1000 | 16.00 | 32768 | 91.9 |" in text
+
+
+def test_hbm_summary_splits_the_trace_by_size(tmp_path):
+    (tmp_path / "out.txt").write_text(
+        "read o (4096 x 4096)   9437184 bytes:      3.38 us per launch,  2792.4 GB/s\n"
+        "read 1 GiB          1073741824 bytes:    188.78 us per launch,  5687.9 GB/s\n")
+    hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    k = "k_read(unsigned int const*, unsigned long, unsigned int*)"
+    durs = [9000, 9000, 9000, 3000, 4000, 5000] + [1000] * 3 + [200000] * 5   # 3 untimed + 3 timed, then 3 + 5
+    rows, t = [], 0
+    for d in durs:
+        rows.append([k, t, t + d])
+        t += d + 100
+    rows.append(["other_kernel()", 0, 10])
+    _csv(str(tmp_path / "tr" / "trace_kernel_trace.csv"), hdr, rows)
+    text = P.hbm_summary(str(tmp_path / "out.txt"), str(tmp_path / "tr"), "cmd", reps=3)
+    assert "| o (4096 x 4096) | 9437184 | 3.38 | 2792.4 | 4.00 | 2359.3 |" in text
+    assert "| 1 GiB | 1073741824 | 188.78 | 5687.9 | 200.00 | 5368.7 |" in text
