@@ -283,6 +283,40 @@ def test_linear_extreme_rows(fmt, group, M):
     check_y(C.host(y), y_ref)
 
 
+def test_calls_on_two_streams_at_once():
+    """The library keeps no device state between calls: two sequences of
+    fused calls (different formats, M and shapes, each call with its own
+    buffers), enqueued alternately on two streams of default priority, give
+    bit for bit what the same calls give one after the other."""
+    cases = [("w4_z16", 64, 16, 4096, 4096), ("w8", 0, 32, 1024, 4096), ("w4_z4", 32, 1, 2048, 1024),
+             ("w4_z16", 128, 1, 4096, 4096)]
+    prepared = []
+    for i, (fmt, g, M, N, K) in enumerate(cases):
+        x, W, signs = synth.random_case(M, N, K, seed=500 + i)
+        prepared.append((C.to_dev(x), C.to_dev(signs), C.gpu_prepare(W, signs, fmt, g)))
+
+    def call(i):
+        xd, sd, w = prepared[i]
+        return C.gpu_fused(xd, sd, w, debug=False)[:3]
+
+    serial = [[C.host(t).copy() for t in call(i)] for i in range(len(cases))]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        torch.cuda.synchronize()
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
+        outs = []
+        for k in range(4):  # A: cases 0, 2, 0, 2; B: cases 1, 3, 1, 3 -- enqueued in turn
+            for j, st in enumerate(streams):
+                i = 2 * (k % 2) + j
+                with torch.cuda.stream(st):
+                    outs.append((i, call(i)))
+        torch.cuda.synchronize()
+        for i, out in outs:
+            for got, ref in zip(out, serial[i]):
+                assert np.array_equal(C.host(got).view(np.uint8), ref.view(np.uint8)), (rep, i)
+
+
 def test_rejects_bad_arguments_without_writing():
     import speculative_verify_gemm_amd as svg
     xq = torch.zeros((2, 64), dtype=torch.int8, device=C.DEV)
