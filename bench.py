@@ -289,6 +289,28 @@ def profiled_traffic(workload, M):
     return float(val.group(1)), os.path.relpath(path, ROOT)
 
 
+def read_kernel_times(workload):
+    """Per launch kind, the time a read-only streaming kernel takes for the
+    same weight bytes, back to back, from the committed calibration summary
+    (speculative_verify_gemm_amd/calib/hbm_read.hip): {kind: us}, or None
+    where the sizes measured are not this workload's (only the W4 g64 stack's
+    launches were)."""
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_read_calibration.md")
+    if workload != "stack_w4g64" or not os.path.exists(path):
+        return None
+    us = {}
+    for m in re.finditer(r"^\| (o|qkv|gate/up) \([^|]*\) \| (\d+) \| ([\d.]+) \|", open(path).read(), re.M):
+        us[m.group(1).replace("/", "")] = (int(m.group(2)), float(m.group(3)))
+    if set(us) != {"o", "qkv", "gateup"}:
+        return None
+    us["down"] = us["qkv"]  # 12288 x 4096 codes and parameters: the same bytes
+    for name, _m, N, K, _s in LAYER_LAUNCHES:
+        if us[name][0] != weight_bytes(N, K, "w4_z16", 64):
+            return None
+    return {name: us[name][1] for name, *_ in LAYER_LAUNCHES}
+
+
 def cpu_model():
     """The host CPU's model name (lscpu's), else the machine type."""
     try:
@@ -523,6 +545,7 @@ def main():
     print(f"[bench] linear launches: mean {kmean_ms * 1e3:.2f} us, {k_gbps:.1f} GB/s; per kind us {kmed}",
           file=sys.stderr, flush=True)
     traffic, traffic_src = profiled_traffic(args.workload, M)
+    read_us = read_kernel_times(args.workload)
     one = stack.fused and one_launch(M, stack.group)
     ops_per_pass = sum(2 * M * N * K for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
     kops = ops_per_pass / (args.layers * len(LAYER_LAUNCHES))  # mean int ops per linear launch
@@ -568,6 +591,12 @@ def main():
                      "int8_tops_kernel": round(kops / (kmean_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_kernel": round(kops / (kmean_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)},
     }
+    if read_us:
+        # the practical ceiling at these sizes: a read-only kernel moving each
+        # launch's weight bytes (same timing method), against the launches
+        out["roofline"]["read_kernel"] = {
+            "us_by_kind": read_us, "source": "profiles/hbm_read_calibration.md",
+            "frac": round(sum(read_us.values()) / sum(kmed.values()), 4)}
     if args.workload != "stack_w8" and M != 1 and not args.no_decode:
         del g
         _io1, g1, (ms1, _med1, _min1), nbytes1 = measure(1)
@@ -586,6 +615,9 @@ def main():
         t16, t1 = sum(kmed.values()), sum(kmed1.values())
         out["linear_only_per_layer"] = {"us_m1": round(t1, 3), f"us_m{M}": round(t16, 3),
                                         "ratio": round(t16 / t1, 4), "m1_by_kind": kmed1}
+        if read_us:
+            out["linear_only_per_layer"]["frac_of_read_kernel_m1"] = round(sum(read_us.values()) / t1, 4)
+            out["linear_only_per_layer"][f"frac_of_read_kernel_m{M}"] = round(sum(read_us.values()) / t16, 4)
         print(f"[bench] linears alone per layer: M=1 {t1:.2f} us, M={M} {t16:.2f} us (x{t16 / t1:.3f})",
               file=sys.stderr, flush=True)
         del g1

@@ -161,3 +161,17 @@ def test_hbm_summary_splits_the_trace_by_size(tmp_path):
     text = P.hbm_summary(str(tmp_path / "out.txt"), str(tmp_path / "tr"), "cmd", reps=3)
     assert "| o (4096 x 4096) | 9437184 | 3.38 | 2792.4 | 4.00 | 2359.3 |" in text
     assert "| 1 GiB | 1073741824 | 188.78 | 5687.9 | 200.00 | 5368.7 |" in text
+
+
+def test_read_kernel_times_match_the_stack_sizes(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    table = ("| size | bytes | us | GB/s | span | GB/s |\n|---|---|---|---|---|---|\n"
+             "| o (4096 x 4096) | 9437184 | 3.38 | 2792.4 | 3.64 | 2592.6 |\n"
+             "| qkv (12288 x 4096) | 28311552 | 6.20 | 4564.6 | 6.32 | 4479.7 |\n"
+             "| gate/up (24576 x 4096) | 56623104 | 10.61 | 5337.6 | 10.76 | 5262.4 |\n")
+    (tmp_path / "profiles" / "hbm_read_calibration.md").write_text(table)
+    assert bench.read_kernel_times("stack_w4g64") == {"qkv": 6.2, "o": 3.38, "gateup": 10.61, "down": 6.2}
+    assert bench.read_kernel_times("stack_w8") is None              # other byte counts
+    (tmp_path / "profiles" / "hbm_read_calibration.md").write_text(table.replace("9437184", "9437185"))
+    assert bench.read_kernel_times("stack_w4g64") is None           # a size that is not the launch's
