@@ -379,7 +379,26 @@ def cpu_baseline(stack, M, min_seconds=12.0, max_reps=32):
             dt += time.perf_counter() - t0
             reps += 1
     nbytes = layer_bytes * reps
-    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+    # the same calls on every core of the process's affinity mask: one worker
+    # thread per core, each taking whole launches (numpy releases the GIL in
+    # its array loops), over the activations of as many layers as workers
+    import concurrent.futures as cf
+    ncores = len(os.sched_getaffinity(0))
+    work = [(synth.stack_acts(stack.wl, L, sp, M), sp, signs, ow)
+            for L in range(ncores) for sp, signs, ow, _N, _K in prepared]
+
+    def one(job):
+        x, _sp, signs, ow = job
+        (O.linear_w8 if stack.fmt == "w8" else O.linear_w4)(x, signs, ow)
+
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=ncores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(one, work))
+        dt_all = time.perf_counter() - t0
+    all_cores = dict(value=layer_bytes * ncores / dt_all / 1e9, threads=ncores, seconds=dt_all,
+                     sample=f"the four launches of layer 0 on the activations of {ncores} layers, "
+                            f"{ncores} worker threads")
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle", all_cores=all_cores,
                 sample=f"the four launches of layer 0 (qkv, o, gate/up, down; {layer_bytes / 1e6:.1f} MB of "
                        f"algorithmic bytes each time) on the activations of {reps} layers at M={M}: "
                        f"activation RHT + int8 quantization, exact integer contraction, fp64 output; "
@@ -648,6 +667,8 @@ def main():
         print("[bench] timing the CPU oracle on layer 0", file=sys.stderr, flush=True)
         cb = cpu_baseline(stack, M)
         out["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
+        out["cpu_baseline"]["all_cores"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                            for k, v in cb["all_cores"].items()}
         if tree_inputs is not None:
             from oracle import tree_oracle as TO
             t0 = time.perf_counter()
