@@ -504,12 +504,102 @@ def time_tree_deltanet(torch, dev, T, H=16, dk=128, dv=128, reps=50):
                 verify_state_GB_per_s=round(state_bytes / (us_v * 1e-6) / 1e9, 2))
 
 
+SINGLE = {
+    "single_1k": "single linear, M=1, K=N=1024, W4 asymmetric g32 (fp16 scale + 4-bit zero), RHT block 32, "
+                 "activations N(0,1) with 4 outlier channels x50",
+    "decode_12k": "decode-sized linear, M=1, K=4096, N=12288, W4 asymmetric g64 (fp16 scale + fp16 zero), "
+                  "RHT block 32, Student-t(3) activations, weights with 0.1% entries x20",
+}
+
+
+def bench_single(args, torch, dev):
+    """One single-matrix workload: the fused call (rotation and quantization of
+    the row, then the contraction, one launch at M = 1) on weight copies that
+    rotate over at least 512 MiB so no launch finds its weights in a cache,
+    all calls of a step captured in one graph; the oracle timed whole on the
+    host.  Returns the JSON object of the bench line."""
+    import numpy as np
+    import synth
+    import speculative_verify_gemm_amd as svg
+    from oracle import svg_oracle as O
+    from speculative_verify_gemm_amd.build import source_digest
+    x, W, signs, spec = synth.single_inputs(args.workload)
+    fmt, group = spec["fmt"], spec["group"]
+    M, K = x.shape
+    N = W.shape[0]
+    sd = torch.from_numpy(signs).to(dev)
+    wq, ws, wz = svg.empty_weights(N, K, fmt, group, device=dev)
+    svg.rht_rotate_weights(torch.from_numpy(W).to(dev), sd, fmt, group, wq, ws, wz)
+    wbytes = weight_bytes(N, K, fmt, group)
+    ncopy = max(2, -(-(512 << 20) // wbytes))
+    copies = [(wq.clone(), ws.clone(), wz.clone()) for _ in range(ncopy)]
+    del wq, ws, wz
+    xd = torch.from_numpy(x).to(dev)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def step():
+        for c in copies:
+            svg.act_quant_w4a8_linear(xd, sd, xq, xs, c[0], c[1], c[2], fmt, group, N, y)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    ms, med, mn = time_graph(torch, g, args.steps, args.warmup, dev)
+    us = ms * 1e3 / ncopy
+    nbytes = linear_bytes(M, N, K, fmt, group)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    print(f"[bench] {args.workload}: {us:.3f} us per call over {ncopy} weight copies, {gbps:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    out = {
+        "metric": "W4A8 linear: achieved HBM GB/s and % of peak at M=1 and M=16 (verify)",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_call": round(us, 3),
+        "us_per_call_median_step": round(med * 1e3 / ncopy, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8xint4",
+        "data": "synthetic (seeded, drawn on the host)", "kernel_digest": source_digest(),
+        "config": {"workload": args.workload, "description": SINGLE[args.workload], "M": M, "N": N, "K": K,
+                   "weight_format": fmt, "group": group, "transform_block": 32, "bytes_per_call": nbytes,
+                   "weight_copies": ncopy, "calls_per_step": ncopy},
+        "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": kernel_name(fmt, group, M, True), "achieved": round(gbps, 2),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "mean_launch_us": round(us, 3)},
+    }
+    read_us = read_kernel_times("stack_w4g64")
+    if read_us and wbytes == weight_bytes(12288, 4096, "w4_z16", 64):  # the calibration's qkv size
+        out["roofline"]["read_kernel"] = {"us": read_us["qkv"], "source": "profiles/hbm_read_calibration.md",
+                                          "frac": round(read_us["qkv"] / us, 4)}
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        ow = O.prepare_w4(W, signs, group)
+        dt, reps = 0.0, 0
+        with threadpool_limits(limits=1):
+            while reps < 64 and (reps == 0 or dt < 10.0):
+                t0 = time.perf_counter()
+                O.linear_w4(x, signs, ow)
+                dt += time.perf_counter() - t0
+                reps += 1
+        out["cpu_baseline"] = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"the whole call {reps} times (activation RHT + int8 "
+                               f"quantization, exact integer contraction, fp64 output); numpy, one thread",
+                               "seconds": round(dt, 3), "cpu": cpu_model()}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stack_w4g64", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="stack_w4g64", choices=sorted(WORKLOADS) + sorted(SINGLE))
     ap.add_argument("--m", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--unfused", action="store_true",
@@ -533,6 +623,9 @@ def main():
     import torch
     from speculative_verify_gemm_amd.build import source_digest
     dev = torch.device("cuda:0")
+    if args.workload in SINGLE:
+        print(json.dumps(bench_single(args, torch, dev)), flush=True)
+        return
     spec = WORKLOADS[args.workload]
     M = args.m or spec["M"]
     print(f"[bench] building {args.workload} ({args.layers} layers) on {torch.cuda.get_device_name(dev)}",
