@@ -616,8 +616,8 @@ def main():
                          "size that scales the HBM byte counters of a profiling run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the linear shards by output rows with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported "
+              "(the linear would shard by output rows, with no exchange inside a launch)", file=sys.stderr)
         sys.exit(2)
 
     import torch
