@@ -17,6 +17,7 @@ torch = pytest.importorskip("torch")
 
 import synth
 from oracle import svg_oracle as O
+from oracle import tree_oracle as TO
 
 pytestmark = pytest.mark.gpu
 
@@ -281,6 +282,78 @@ def test_linear_extreme_rows(fmt, group, M):
     assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
+
+
+def _banded(shape, dtype, fill, pad=4096):
+    """A device buffer with `pad` elements of `fill` on both sides of a view
+    of `shape` (the pad keeps 16-byte alignment for every dtype used)."""
+    n = int(np.prod(shape))
+    buf = torch.full((pad + n + pad,), fill, dtype=dtype, device=C.DEV)
+    return buf, buf[pad:pad + n].view(*shape), pad
+
+
+def _bands_intact(buf, pad, n, fill):
+    b = C.host(buf)
+    return bool(np.all(b[:pad] == fill) and np.all(b[pad + n:] == fill))
+
+
+@pytest.mark.parametrize("fmt,group,M,N,K", [("w4_z16", 64, 1, 100, 4096), ("w4_z16", 64, 16, 100, 4096),
+                                             ("w8", 0, 32, 70, 1024), ("w4_z4", 32, 3, 50, 96),
+                                             ("w4_z16", 128, 1, 33, 12288)])
+def test_guard_bands_of_the_fused_call(fmt, group, M, N, K):
+    """Canary bytes around xq, x_scale and y stay untouched by the fused call
+    (one launch at M = 1, where workgroup 0 writes xq and x_scale; two
+    otherwise), and the outputs between them equal a plain call's."""
+    import speculative_verify_gemm_amd as svg
+    x, W, signs = synth.random_case(M, N, K, seed=600 + M + N)
+    w = C.gpu_prepare(W, signs, fmt, group)
+    ref = [C.host(t).copy() for t in C.gpu_fused(x, signs, w, debug=False)[:3]]
+    bq, xq, pq = _banded((M, K), torch.int8, 77)
+    bs, xs, ps = _banded((M,), torch.float32, 12345.0)
+    by, y, py = _banded((M, N), torch.float32, 12345.0)
+    xd, sd = C.to_dev(x), C.to_dev(signs)
+    if fmt == "w8":
+        svg.act_quant_w8a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], N, y)
+    else:
+        svg.act_quant_w4a8_linear(xd, sd, xq, xs, w["wq"], w["ws"], w["wz"], fmt, group, N, y)
+    assert _bands_intact(bq, pq, M * K, 77)
+    assert _bands_intact(bs, ps, M, 12345.0)
+    assert _bands_intact(by, py, M * N, 12345.0)
+    for got, r in zip((xq, xs, y), ref):
+        assert np.array_equal(C.host(got).view(np.uint8), r.view(np.uint8))
+
+
+def test_guard_bands_of_the_tree_calls():
+    """Canary words around the outputs of tree_accept_greedy (target, path,
+    emit, n_emit) and tree_deltanet_verify (out), and around the state that
+    tree_deltanet_commit rewrites in place."""
+    import speculative_verify_gemm_amd as svg
+    from oracle import deltanet_oracle as DN
+    T, V = 12, 5000
+    logits, parent, draft = synth.draft_tree(T, V, seed=61, accept=5, ties=True)
+    outs = [_banded((T,), torch.int32, -12345) for _ in range(3)] + [_banded((1,), torch.int32, -12345)]
+    svg.tree_accept_greedy(C.to_dev(logits), C.to_dev(parent.astype(np.int32)), C.to_dev(draft.astype(np.int32)),
+                           outs[0][1], outs[1][1], outs[2][1], outs[3][1], svg.tree_workspace())
+    for (buf, _v, pad), n in zip(outs, (T, T, T, 1)):
+        assert _bands_intact(buf, pad, n, -12345)
+    H, dk, dv = 3, 64, 128
+    S0, q, k, v, a, b, par = synth.deltanet_case(T, H, dk, dv, seed=62)
+    ob, out, po = _banded((T, H, dv), torch.float32, 12345.0)
+    sb, state, ps = _banded((H, dv, dk), torch.float32, 12345.0)
+    state.copy_(C.to_dev(S0))
+    devs = [C.to_dev(t) for t in (q, k, v, a, b)]
+    svg.tree_deltanet_verify(state, *devs, C.to_dev(par.astype(np.int32)), out)
+    assert _bands_intact(ob, po, T * H * dv, 12345.0)
+    path = [int(n) for n in TO.root_path(par, T - 1)[1:]]
+    pd = torch.full((T,), -1, dtype=torch.int32, device=C.DEV)
+    if path:
+        pd[:len(path)] = C.to_dev(np.array(path, np.int32))
+    svg.tree_deltanet_commit(state, devs[1], devs[2], devs[3], devs[4], pd,
+                             torch.tensor([len(path) + 1], dtype=torch.int32, device=C.DEV))
+    assert _bands_intact(sb, ps, H * dv * dk, 12345.0)
+    ref = DN.tree_commit(S0, q, k, v, a, b, par, path)
+    got = C.host(state)
+    assert np.max(np.abs(got - ref)) <= 1e-4 * (np.max(np.abs(ref)) + 1.0)
 
 
 def test_calls_on_two_streams_at_once():
