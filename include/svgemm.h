@@ -118,7 +118,8 @@ svg_status svg_weight_sizes(int N, int K, int fmt, int group, uint64_t* wq_bytes
  *  Per row, u = H_B . diag(signs) . W[n] blockwise (butterfly stages
  *  h = 1, 2, 4, ..., B/2 in that order).  W4 per group: lo = min(0, min u),
  *  hi = max(0, max u), s = fp16(rne((hi - lo) / 15)) (1.0 if zero),
- *  z = rint(-lo / s), q = clamp(rint(u / s) + z, 0, 15).  W8 per row:
+ *  z = clamp(rint(-lo / s), 0, 15) (a 4-bit unsigned value; -lo / s passes
+ *  15 only when s is an fp16 subnormal), q = clamp(rint(u / s) + z, 0, 15).  W8 per row:
  *  s = fp16(rne(max|u| / 127)) (1.0 if zero), q = clamp(rint(u / s), -127, 127).
  *  Matrices whose rows are stacked along N (e.g. the q, k and v projections)
  *  may be rotated one at a time into consecutive 16-row tiles of one buffer

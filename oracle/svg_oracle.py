@@ -28,7 +28,7 @@ What the pages fix, and the readings taken where they are silent:
   that order, every add/sub one fp32 round-to-nearest-even operation; per-token
   symmetric int8 activations with codes in [-127, 127]; min/max asymmetric W4
   per group along K with the range widened to contain 0, fp16 scale, integer
-  zero point in [0, 15]; per-output-row symmetric W8 with fp16 scale.
+  zero point clamped to [0, 15] (a 4-bit unsigned value); per-output-row symmetric W8 with fp16 scale.
 * A second transform block, 64 (the width of one CDNA wave, where the pages'
   32 is the width of the SIMD group of the hardware they target), is a
   variant: the same butterfly with one more stage (h = 32) and the combined
@@ -130,7 +130,9 @@ def act_quant_i8(u: np.ndarray, block: int = BLOCK):
     safe = np.where(amax > 0, sigma, F32(1))
     q = np.clip(np.rint(u / safe[..., None]), -127, 127)
     q = np.where(amax[..., None] > 0, q, F32(0)).astype(np.int8)
-    scale = (sigma * F32(1.0 / block)).astype(F32)  # exact: block is a power of two
+    # a power-of-two factor: exact, except where sigma / block falls below the
+    # normal range and rounds like any fp32 product
+    scale = (sigma * F32(1.0 / block)).astype(F32)
     return q, scale
 
 
@@ -142,7 +144,9 @@ def quant_w4(u: np.ndarray, group: int):
     asymmetric integer quantization; every value of a group shares one scale].
 
     Per group: lo = min(0, min u), hi = max(0, max u); s = fp16(rne((hi - lo) /
-    15)), replaced by 1.0 if zero; z = rint(-lo / s) in [0, 15];
+    15)), replaced by 1.0 if zero; z = clamp(rint(-lo / s), 0, 15) -- the zero
+    point is an unsigned 4-bit integer, and -lo / s can pass 15 when s lands in
+    fp16's subnormal range, where its relative rounding is coarse;
     q = clamp(rint(u / s) + z, 0, 15).  Returns (q uint8 [N, K] in 0..15,
     s fp16 [N, K/group], z uint8 [N, K/group])."""
     u = np.asarray(u, dtype=F32)
@@ -155,7 +159,7 @@ def quant_w4(u: np.ndarray, group: int):
     s = ((hi - lo) / F32(15)).astype(np.float16)
     s = np.where(s == 0, np.float16(1.0), s).astype(np.float16)
     s32 = s.astype(F32)
-    z = np.rint(-lo / s32)
+    z = np.clip(np.rint(-lo / s32), 0, 15)
     q = np.clip(np.rint(ug / s32[..., None]) + z[..., None], 0, 15)
     return q.reshape(N, K).astype(np.uint8), s, z.astype(np.uint8)
 

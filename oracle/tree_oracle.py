@@ -9,9 +9,9 @@ Source: "Karpathy's Trick for Faster Local LLMs Finally Has Proper Tooling"
 pass": the main model checks all drafted positions in one pass, keeps the
 valid prefix and goes on from the first rejected position with its own token;
 five drafted tokens of which it agrees with the first four advance the
-sequence by five.  Section "Issue with parallel draft generation": when the
-drafts form a tree of alternative continuations, the main model verifies the
-tree and accepts the longest valid path.
+sequence by five.  Section "Issue with parallel draft generation": with a
+tree of alternative drafted continuations, what is kept is the deepest root
+path whose every edge the target agrees with.
 
 The pages give no procedure beyond that.  Readings taken here:
 

@@ -143,7 +143,9 @@ __global__ __launch_bounds__(kThreads) void k_rot_quant_w4(const float* __restri
     __half sh = __float2half_rn((hi - lo) / 15.0f);
     if (__half_as_ushort(sh) == 0) sh = __ushort_as_half(0x3C00);  // 1.0
     const float s = __half2float(sh);
-    const int z = valid ? (int)rintf(-lo / s) : 0;
+    // the zero point is a 4-bit unsigned value: -lo / s passes 15 when s
+    // falls in fp16's subnormal range, whose steps are coarse
+    const int z = valid ? clamp_i((int)rintf(-lo / s), 0, 15) : 0;
     const int q0 = clamp_i((int)rintf(e0 / s) + z, 0, 15);
     const int q1 = clamp_i((int)rintf(e1 / s) + z, 0, 15);
     const int q2 = clamp_i((int)rintf(e2 / s) + z, 0, 15);

@@ -5,8 +5,8 @@
 // pass": the main model checks all drafted positions in one pass, keeps the
 // valid prefix and goes on from the first rejected position with its own
 // token (five drafted, the first four agreed: the sequence advances by five).
-// Section "Issue with parallel draft generation": with a tree of drafts the
-// main model accepts the longest valid path.  The readings (include/svgemm.h,
+// Section "Issue with parallel draft generation": over a tree of drafts,
+// the deepest root path that agrees at every edge is kept.  The readings (include/svgemm.h,
 // tree_accept_greedy): node 0 is the root, parent[i] < i; the target's choice
 // at a node is the first largest logit of its row; a node is valid when its
 // parent is valid and its token is the parent's choice; the deepest valid node
@@ -18,7 +18,8 @@
 //     (order-preserving bits of the value) << 32 | (2^32 - 1 - index), so that
 //     the largest key is the largest value and, among equal values, the
 //     smallest index; it folds the key into its row's slot of the workspace
-//     with a 64-bit atomic max, then counts itself in its row (the workgroup
+//     with a 64-bit atomic max, then -- with an operand that depends on the
+//     max's returned value -- counts itself in its row (the workgroup
 //     completing a row counts the row in).
 //  2. The workgroup completing the last row reads the row keys (every
 //     workgroup's key was acknowledged before it counted itself), clears the
@@ -104,15 +105,19 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept(const float* __restric
     u64 b = wave_best[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = umax64(b, wave_best[w]);
-    __hip_atomic_fetch_max(keys + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const u64 old = __hip_atomic_fetch_max(keys + row, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The key is performed at the device's coherence point before this
-    // workgroup counts itself: wait for its acknowledgement (no cache-wide
-    // write-back is needed, nothing else was written).  The count goes to the
-    // row first, and only the workgroup completing a row counts the row in,
-    // so no single word takes every workgroup's atomic.
-    __builtin_amdgcn_s_waitcnt(0);
+    // workgroup counts itself: the count's operand depends on the value the
+    // max returned (an opaque zero made from it), so neither the compiler nor
+    // the hardware can issue the count before the max has been performed --
+    // no cache-wide write-back is needed, nothing else was written.  The
+    // count goes to the row first, and only the workgroup completing a row
+    // counts the row in, so no single word takes every workgroup's atomic.
+    u32 after_key = (u32)old;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(after_key) : "0"(after_key));
     int done = 0;
-    if (__hip_atomic_fetch_add(row_count + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (u32)S - 1)
+    if (__hip_atomic_fetch_add(row_count + row, 1u + after_key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        (u32)S - 1)
       done = __hip_atomic_fetch_add(rows_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (u32)T - 1;
     last = done;
   }

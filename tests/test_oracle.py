@@ -523,6 +523,153 @@ def test_output_error_metric():
     assert e == 0 and abs(r - 2e-3) < 1e-12
 
 
+# ------------------------------------------- exact-rounding pins (brute force)
+# Every integer code of the method is decided by one binary32 operation (or
+# the binary16 conversion of a scale) followed by round-half-to-even.  The
+# pins below recompute those decisions in exact rational arithmetic with the
+# rounding done by integer code (oracle/brute.py), on tiny rows and groups
+# built to sit on the decisions: exact half-integer quotients, quotients one
+# ulp either side of a half-integer (where u * (1/sigma) and u / sigma part),
+# scales in binary16's subnormal range, and butterflies whose result depends
+# on the order of the stages.
+def _fr(a):
+    return Fraction(float(a))
+
+
+def _near_half_row(amax, K=1024):
+    """A rotated row of maximum |u| = amax whose other values lie on and one or
+    two ulps either side of (n + 1/2) * sigma for n = 0..126 (both signs), where
+    sigma = fl32(amax / 127): the quotients u / sigma sit at or next to
+    half-integers."""
+    amax = np.float32(amax)
+    sigma = Fraction(brute.f32(_fr(amax) / 127))
+    vals = [amax]
+    for n in range(127):
+        c = np.float32(float(brute.f32((n + Fraction(1, 2)) * sigma)))
+        for d in (-2, -1, 0, 1, 2):
+            u = c
+            for _ in range(abs(d)):
+                u = np.nextafter(u, np.float32(np.inf) if d > 0 else np.float32(-np.inf))
+            if abs(u) <= amax:
+                vals.append(u if n % 2 else -u)
+    vals = vals[:K]
+    row = np.zeros(K, np.float32)
+    row[:len(vals)] = vals
+    return row
+
+
+def _exact_tie_row():
+    """amax = 127 gives sigma = 1 exactly, so every x.5 value is an exact tie."""
+    vals = [127.0, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 3.5, 64.5, -64.5, 125.5, -126.5, 126.5, 0.25, -0.75]
+    row = np.zeros(64, np.float32)
+    row[:len(vals)] = vals
+    return row
+
+
+def _act_rows():
+    rng = np.random.default_rng(31)
+    rows = [_exact_tie_row(), _near_half_row(3.7), _near_half_row(0.011), _near_half_row(2.0e30),
+            _near_half_row(1.0e-38)]
+    K = max(r.size for r in rows)
+    out = np.zeros((len(rows) + 3, K), np.float32)
+    for i, r in enumerate(rows):
+        out[i, :r.size] = r
+    out[len(rows)] = rng.standard_normal(K).astype(np.float32)
+    out[len(rows) + 1] = (rng.standard_t(3, K) * 1e-41).astype(np.float32)   # subnormal row
+    return out                                                                  # last row: zeros
+
+
+def test_act_quant_matches_exact_rounding():
+    u = _act_rows()
+    q, sc = O.act_quant_i8(u)
+    for m in range(u.shape[0]):
+        codes, scale = brute.act_quant_row_exact([_fr(a) for a in u[m]])
+        assert q[m].tolist() == codes, m
+        assert _fr(sc[m]) == scale, m
+    # the tie row lands where round-half-to-even puts it
+    assert q[0, 1:12].tolist() == [0, 0, 2, -2, 2, -2, 4, 64, -64, 126, -126]
+
+
+def _w4_groups(group):
+    """Tiny groups on the W4 quantizer's decisions (one row of K = 8 groups)."""
+    rng = np.random.default_rng(group)
+    g = []
+    # s = 1 exactly (hi - lo = 15): exact ties in the codes and in the zero point
+    tie = np.zeros(group, np.float32)
+    tie[:8] = [-6.5, 8.5, 0.5, -0.5, 2.5, -2.5, 1.5, 4.5]
+    g.append(tie)
+    # one-sided groups whose scale falls in binary16's subnormal range (steps
+    # of 2^-24): (hi - lo) / 15 = 1.49 and 2.4 steps round to s = 1 and 2
+    # steps, so -lo / s = 22.35 and 18 pass 15 and the 4-bit zero point is
+    # clamped; then random one-sided groups of such ranges
+    for lo_steps in (22.35, 36.0):
+        g.append(np.linspace(-lo_steps * 2.0 ** -24, 0.0, group).astype(np.float32))
+    for r in (1e-6, 3e-7, 1e-5):
+        g.append((-np.abs(rng.standard_normal(group)) * r).astype(np.float32))
+    g.append((np.abs(rng.standard_normal(group)) * 1e-6).astype(np.float32))    # lo = 0
+    g.append(np.zeros(group, np.float32))                                        # s falls back to 1
+    g.append(np.full(group, 1e-9, np.float32))                                   # s underflows to 0 -> 1
+    g.append((rng.standard_normal(group) * 0.5).astype(np.float32))
+    return np.concatenate(g)[None, :]
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_w4_quant_matches_exact_rounding(group):
+    u = _w4_groups(group)
+    q, s, z = O.quant_w4(u, group)
+    G = u.shape[1] // group
+    clamped = 0
+    for j in range(G):
+        grp = [_fr(a) for a in u[0, j * group:(j + 1) * group]]
+        codes, sb, zb = brute.w4_group_exact(grp)
+        assert q[0, j * group:(j + 1) * group].tolist() == codes, j
+        assert _fr(s[0, j]) == sb and int(z[0, j]) == zb, j
+        lo = min(Fraction(0), min(grp))
+        clamped += rne_unclamped_zero(lo, sb) > 15
+    assert clamped >= 2          # the subnormal-scale groups do need the clamp
+    assert z.max() <= 15
+    # the tie group: s = 1, z = rne(6.5) = 6, codes rne(u) + 6
+    assert float(s[0, 0]) == 1.0 and z[0, 0] == 6
+    assert q[0, :8].tolist() == [0, 14, 6, 6, 8, 4, 8, 10]
+
+
+def rne_unclamped_zero(lo, s):
+    return brute.rne(brute.f32(-lo / s))
+
+
+def test_w8_quant_matches_exact_rounding():
+    rng = np.random.default_rng(8)
+    rows = np.zeros((6, 96), np.float32)
+    rows[0, :9] = [127.0, 2.5, -2.5, 3.5, -126.5, 0.5, 1.5, -0.5, 64.5]   # s = 1: exact ties
+    rows[1] = _near_half_row(5.3, 96)
+    rows[2] = (rng.standard_t(3, 96) * 1e-4).astype(np.float32)            # subnormal fp16 scale
+    rows[3] = (rng.standard_normal(96) * 1e-9).astype(np.float32)          # scale underflows -> 1
+    rows[4] = rng.standard_normal(96).astype(np.float32)                   # row 5: zeros
+    q, s = O.quant_w8(rows)
+    for n in range(rows.shape[0]):
+        codes, sb = brute.w8_row_exact([_fr(a) for a in rows[n]])
+        assert q[n].tolist() == codes, n
+        assert _fr(s[n]) == sb, n
+    assert q[0, :9].tolist() == [127, 2, -2, 4, -126, 0, 2, 0, 64]
+
+
+@pytest.mark.parametrize("block", [32, 64])
+def test_fwht_fp32_matches_scalar_butterfly(block):
+    # N(0, 1) blocks and blocks mixing magnitudes 2^-20 .. 2^20: in fp32 the
+    # result depends on the order of the stages (a butterfly run h = 16 .. 1
+    # changes most values), so this fixes the ascending order bit for bit.
+    rng = np.random.default_rng(block)
+    K = 4 * block
+    x = rng.standard_normal((2, K)).astype(np.float32)
+    x[1] *= (2.0 ** rng.integers(-20, 21, K)).astype(np.float32)
+    s = synth.rademacher(K, rng)
+    u = O.rht(x, s, np.float32, block)
+    for r in range(2):
+        for b0 in range(0, K, block):
+            ref = brute.fwht_f32([_fr(x[r, k]) * int(s[k]) for k in range(b0, b0 + block)])
+            assert [_fr(a) for a in u[r, b0:b0 + block]] == ref, (r, b0)
+
+
 # ------------------------------------------------- planted-mistake check
 def test_planted_mistakes_are_caught(monkeypatch):
     """Plant plausible slips in the oracle (on the CPU) and check that the
@@ -589,7 +736,89 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as mp:
         mp.setattr(O, "quant_w4", quant_w4_zero_sign)
         caught.append(_fails(lambda: test_w4_quant_bounds(64)))
+    # rounding slips: half away from zero, a reciprocal multiply instead of the
+    # IEEE quotient, the butterfly's stages in descending order, and the zero
+    # point left unclamped
+    def round_half_away(v):
+        return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+    def act_quant_half_away(u, block=32):
+        u = np.asarray(u, np.float32)
+        amax = np.max(np.abs(u), axis=-1)
+        sigma = amax / np.float32(127)
+        safe = np.where(amax > 0, sigma, np.float32(1))
+        q = np.clip(round_half_away(u / safe[..., None]), -127, 127)
+        q = np.where(amax[..., None] > 0, q, 0).astype(np.int8)
+        return q, (sigma * np.float32(1.0 / block)).astype(np.float32)
+
+    def act_quant_reciprocal(u, block=32):
+        u = np.asarray(u, np.float32)
+        amax = np.max(np.abs(u), axis=-1)
+        sigma = amax / np.float32(127)
+        safe = np.where(amax > 0, sigma, np.float32(1))
+        with np.errstate(all="ignore"):  # 1 / sigma overflows on the subnormal row
+            rinv = (np.float32(1) / safe).astype(np.float32)
+            q = np.clip(np.nan_to_num(np.rint(u * rinv[..., None])), -127, 127)
+        q = np.where(amax[..., None] > 0, q, 0).astype(np.int8)
+        return q, (sigma * np.float32(1.0 / block)).astype(np.float32)
+
+    def quant_w4_with(round_fn, clamp_zero):
+        def quant(u, group):
+            u = np.asarray(u, np.float32)
+            N, K = u.shape
+            ug = u.reshape(N, K // group, group)
+            lo = np.minimum(np.float32(0), ug.min(axis=-1))
+            hi = np.maximum(np.float32(0), ug.max(axis=-1))
+            s = ((hi - lo) / np.float32(15)).astype(np.float16)
+            s = np.where(s == 0, np.float16(1.0), s).astype(np.float16)
+            s32 = s.astype(np.float32)
+            z = round_fn(-lo / s32)
+            if clamp_zero:
+                z = np.clip(z, 0, 15)
+            q = np.clip(round_fn(ug / s32[..., None]) + z[..., None], 0, 15)
+            return q.reshape(N, K).astype(np.uint8), s, z.astype(np.int64)
+        return quant
+
+    def fwht_descending(v, block=32):
+        v = np.array(v, copy=True)
+        b = v.reshape(-1, v.shape[-1] // block, block)
+        h = block // 2
+        while h >= 1:
+            lo = [i for i in range(block) if not i & h]
+            hi = [i + h for i in lo]
+            a, c = b[:, :, lo], b[:, :, hi]
+            b[:, :, lo] = a + c
+            b[:, :, hi] = a - c
+            h //= 2
+        return b.reshape(v.shape)
+
+    rounding = []
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "act_quant_i8", act_quant_half_away)
+        rounding.append(_fails(test_act_quant_matches_exact_rounding))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "act_quant_i8", act_quant_reciprocal)
+        rounding.append(_fails(test_act_quant_matches_exact_rounding))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "quant_w4", quant_w4_with(round_half_away, True))
+        rounding.append(_fails(lambda: test_w4_quant_matches_exact_rounding(64)))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "quant_w4", quant_w4_with(np.rint, False))
+        rounding.append(_fails(lambda: test_w4_quant_matches_exact_rounding(32)))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "fwht32", lambda v: fwht_descending(v, 32))
+        rounding.append(_fails(lambda: test_fwht_fp32_matches_scalar_butterfly(32)))
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "fwht", fwht_descending)
+        rounding.append(_fails(lambda: test_fwht_fp32_matches_scalar_butterfly(64)))
+    # the pins these slips used to pass are blind to them (integer and unit
+    # inputs are exact in any order; the bounds hold for either rounding)
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "fwht32", lambda v: fwht_descending(v, 32))
+        blind = not _fails(lambda: test_rotation_matches_explicit_product_on_integers(96))
     assert all(caught), caught
+    assert all(rounding), rounding
+    assert blind
 
 
 def _fails(fn):

@@ -263,7 +263,8 @@ def test_weight_codes_extreme_rows(fmt, group):
         assert np.array_equal(C.host(w["wz"]).view(np.uint8), wz.view(np.uint8).reshape(-1))
 
 
-@pytest.mark.parametrize("fmt,group,M", [("w4_z16", 64, 1), ("w4_z16", 64, 16), ("w8", 0, 32)])
+@pytest.mark.parametrize("fmt,group,M", [("w4_z16", 64, 1), ("w4_z16", 64, 16), ("w8", 0, 32),
+                                         ("w4_z4", 32, 3), ("w4_z4", 64, 16)])
 def test_linear_extreme_rows(fmt, group, M):
     """The whole call on rows of very different magnitudes (activations from
     1e-20 to 1e20, weights from fp16-subnormal scales to 1e3), with every
@@ -280,6 +281,36 @@ def test_linear_extreme_rows(fmt, group, M):
     w = C.gpu_prepare(W, signs, fmt, group)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
     assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
+    check_y(C.host(y), y_ref)
+
+
+@pytest.mark.parametrize("fmt,group,M", [("w4_z4", 32, 1), ("w4_z4", 64, 16), ("w4_z16", 128, 2),
+                                         ("w4_z16", 64, 16)])
+def test_zero_point_clamp(fmt, group, M):
+    """One-sided weight groups (every value <= 0) of ranges 1e-7 .. 1e-5,
+    where the fp16 scale is subnormal and -lo / s passes 15: the 4-bit zero
+    point is clamped to 15 (no carry into the neighbouring group's nibble in
+    the 4-bit zero format).  Codes, scales and zeros bit-exact; partial sums
+    bit-exact; y within tolerance."""
+    N, K = 48, 512
+    C.say(f"zero-point clamp fmt={fmt} g={group} M={M}")
+    x, W, signs = synth.random_case(M, N, K, seed=90 + M + group)
+    ranges = np.resize([1e-7, 3e-7, 1e-6, 3e-6, 1e-5, 1.0], N).astype(np.float32)
+    W = -np.abs(_scaled_rows(W, ranges))
+    u = O.rht(W, signs)
+    # fold the signs back so the rotated rows themselves are one-sided: W = D H^T u / 32
+    target = -np.abs(u)
+    W = (O.fwht32(target.astype(np.float64)) * signs.astype(np.float64) / 32.0).astype(np.float32)
+    ow = O.prepare_w4(W, signs, group)
+    assert ow["z"].max() == 15
+    y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
+    w = C.gpu_prepare(W, signs, fmt, group)
+    wq, ws, wz = C.oracle_storage(ow, fmt, K)
+    assert np.array_equal(C.host(w["wq"]).view(np.uint8), wq.view(np.uint8).reshape(-1))
+    assert np.array_equal(C.host(w["ws"]).view(np.uint16), ws.view(np.uint16).reshape(-1))
+    assert np.array_equal(C.host(w["wz"]).view(np.uint8), wz.view(np.uint8).reshape(-1))
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
 
