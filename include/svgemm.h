@@ -271,6 +271,26 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
                               int32_t* n_emit, void* workspace, void* stream);
 
 /*
+ * tree_accept_greedy_static -- tree_accept_greedy without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid hipMalloc).  It allocates nothing: the
+ * workspace is the library's own static device array of
+ * SVG_TREE_WORKSPACE_BYTES (512) bytes, one per device, held until the process
+ * ends.  The first call on a device looks its address up and zero-fills it
+ * with a small kernel enqueued on `stream` ahead of the call's own kernel;
+ * every call leaves it zero-filled again.  All calls on one device share it:
+ * calls that may overlap on one device (other streams, other threads) race
+ * and must not be made; use tree_accept_greedy with separate workspaces then.
+ *  Arguments and outputs as for tree_accept_greedy.  T above
+ *  SVG_TREE_MAX_NODES (32), the limit the array is sized for, is
+ *  SVG_EUNSUPPORTED; a failure to find the array on the current device is
+ *  SVG_EHIP.
+ */
+svg_status tree_accept_greedy_static(const float* logits, int T, int V, const int32_t* parent,
+                                     const int32_t* draft, int32_t* target, int32_t* path,
+                                     int32_t* emit, int32_t* n_emit, void* stream);
+
+/*
  * tree_deltanet_verify, tree_deltanet_commit -- a fixed-state recurrent layer
  * over a draft tree, without restoring state.
  * [KT "Verifying a draft tree without restoring model state": a Gated

@@ -44,10 +44,12 @@ def _load():
     lib.act_quant_w4a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.act_quant_w8a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, i, vp, vp, vp]
     lib.tree_accept_greedy.argtypes = [vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.tree_accept_greedy_static.argtypes = [vp, i, i, vp, vp, vp, vp, vp, vp, vp]
     lib.tree_deltanet_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp]
     lib.tree_deltanet_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
     for fn in (lib.rht_rotate_weights, lib.act_rht_quant_i8, lib.w4a8_linear, lib.w8a8_linear,
                lib.act_quant_w4a8_linear, lib.act_quant_w8a8_linear, lib.tree_accept_greedy,
+               lib.tree_accept_greedy_static,
                lib.tree_deltanet_verify, lib.tree_deltanet_commit):
         fn.restype = ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
@@ -251,6 +253,15 @@ def tree_accept_greedy(logits, parent, draft, target, path, emit, n_emit, worksp
     """Greedy acceptance of a verified draft tree (include/svgemm.h): logits
     [T, V] fp32; parent, draft [T] int32; outputs target, path, emit [T] and
     n_emit [1] int32; workspace from tree_workspace()."""
+    T, V = _tree_args(logits, parent, draft, target, path, emit, n_emit)
+    _dev(workspace, "workspace", torch.uint8)
+    if workspace.numel() < TREE_WORKSPACE_BYTES:
+        raise ValueError("workspace needs TREE_WORKSPACE_BYTES bytes")
+    _check(lib.tree_accept_greedy(_p(logits), T, V, _p(parent), _p(draft), _p(target), _p(path),
+                                  _p(emit), _p(n_emit), _p(workspace), _stream(stream, logits)))
+
+
+def _tree_args(logits, parent, draft, target, path, emit, n_emit):
     _dev(logits, "logits", torch.float32)
     T, V = logits.shape
     for name, t in (("parent", parent), ("draft", draft), ("target", target), ("path", path),
@@ -259,11 +270,17 @@ def tree_accept_greedy(logits, parent, draft, target, path, emit, n_emit, worksp
         if tuple(t.shape) != (T,):
             raise ValueError(f"{name} must have shape [{T}]")
     _dev(n_emit, "n_emit", torch.int32)
-    _dev(workspace, "workspace", torch.uint8)
-    if n_emit.numel() < 1 or workspace.numel() < TREE_WORKSPACE_BYTES:
-        raise ValueError("n_emit needs 1 element and workspace TREE_WORKSPACE_BYTES bytes")
-    _check(lib.tree_accept_greedy(_p(logits), T, V, _p(parent), _p(draft), _p(target), _p(path),
-                                  _p(emit), _p(n_emit), _p(workspace), _stream(stream, logits)))
+    if n_emit.numel() < 1:
+        raise ValueError("n_emit needs 1 element")
+    return T, V
+
+
+def tree_accept_greedy_static(logits, parent, draft, target, path, emit, n_emit, stream=None):
+    """tree_accept_greedy on the library's own static workspace (nothing
+    allocated; calls that may overlap on one device must not be made)."""
+    T, V = _tree_args(logits, parent, draft, target, path, emit, n_emit)
+    _check(lib.tree_accept_greedy_static(_p(logits), T, V, _p(parent), _p(draft), _p(target), _p(path),
+                                         _p(emit), _p(n_emit), _stream(stream, logits)))
 
 
 def _gdn_shapes(state, k, v, alpha, beta):

@@ -30,6 +30,9 @@ hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K,
 hipError_t svg_launch_tree_accept(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,
                                   int32_t* target, int32_t* path, int32_t* emit, int32_t* n_emit, void* workspace,
                                   hipStream_t stream);
+// The device address of the library's own tree workspace on the current
+// device (set up and zero-filled on `stream` at the first call per device).
+hipError_t svg_tree_scratch(hipStream_t stream, void** out);
 
 // Gated delta-rule layer over a draft tree (tree_deltanet.hip).  Head sizes:
 // d_k in {64, 128}, d_v in {64, 128, 256}.

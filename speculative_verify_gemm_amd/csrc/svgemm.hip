@@ -1,6 +1,7 @@
 // C ABI entry points (include/svgemm.h): host-side validation, then one
 // enqueue on the caller's stream.  No allocation, no synchronisation, no state
-// shared between calls apart from the per-thread error text.
+// shared between calls apart from the per-thread error text and the static
+// workspace of tree_accept_greedy_static (one per device, tree_accept.hip).
 #include "../../include/svgemm.h"
 
 #include <stdint.h>
@@ -271,6 +272,24 @@ svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* 
   if (!aligned(workspace, 8)) return fail(SVG_EALIGN, fn, "workspace must be 8-byte aligned");
   return hip_status(fn, svg_launch_tree_accept(logits, T, V, parent, draft, target, path, emit, n_emit, workspace,
                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status tree_accept_greedy_static(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,
+                                     int32_t* target, int32_t* path, int32_t* emit, int32_t* n_emit, void* stream) {
+  static const char* fn = "tree_accept_greedy_static";
+  if (!logits || !parent || !draft || !target || !path || !emit || !n_emit)
+    return fail(SVG_EINVAL, fn, "null pointer");
+  if (T < 1 || V < 1) return fail(SVG_EINVAL, fn, "T and V must be >= 1");
+  if (T > SVG_TREE_MAX_NODES) return fail(SVG_EUNSUPPORTED, fn, "T > SVG_TREE_MAX_NODES (the static workspace's limit)");
+  if (V > kMaxV) return fail(SVG_EUNSUPPORTED, fn, "V > 2^30");
+  if (!aligned(logits, 4) || !aligned(parent, 4) || !aligned(draft, 4) || !aligned(target, 4) || !aligned(path, 4) ||
+      !aligned(emit, 4) || !aligned(n_emit, 4))
+    return fail(SVG_EALIGN, fn, "logits, parent, draft and the outputs must be 4-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  hipError_t e = svg_tree_scratch(s, &ws);
+  if (e != hipSuccess) return hip_status(fn, e);
+  return hip_status(fn, svg_launch_tree_accept(logits, T, V, parent, draft, target, path, emit, n_emit, ws, s));
 }
 
 svg_status tree_deltanet_verify(const float* state, const float* q, const float* k, const float* v,

@@ -29,7 +29,9 @@
 // Nothing waits for another workgroup, so no launch order or residency is
 // assumed.
 #include <algorithm>
+#include <mutex>
 
+#include "../../include/svgemm.h"
 #include "svg_device.h"
 #include "svg_internal.h"
 
@@ -186,6 +188,50 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept(const float* __restric
 }
 
 }  // namespace
+
+// ------------------------------------------------ the library's own workspace
+// For callers that cannot allocate (code under stream capture, serving loops
+// that forbid hipMalloc): one workspace per device in a static device array,
+// shared by every call on that device.  Each call leaves it zero-filled, as
+// it found it; calls that overlap on one device race on it.  In host code the
+// array's name is not a device address: its address on the current device
+// comes from hipGetSymbolAddress, once per device, and only that is used.
+static __device__ __align__(256) unsigned char scratch[SVG_TREE_WORKSPACE_BYTES];
+
+namespace {
+
+__global__ __launch_bounds__(64) void k_zero_scratch(u32* p, int nwords) {
+  for (int i = threadIdx.x; i < nwords; i += 64) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // the array's device address, per device (null until set up)
+
+}  // namespace
+
+hipError_t svg_tree_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // start from zeros once, with a kernel on the caller's stream (ahead of
+    // its first use there; no memset node if the caller is capturing)
+    hipLaunchKernelGGL(k_zero_scratch, dim3(1), dim3(64), 0, stream, static_cast<u32*>(p),
+                       SVG_TREE_WORKSPACE_BYTES / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 hipError_t svg_launch_tree_accept(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,
                                   int32_t* target, int32_t* path, int32_t* emit, int32_t* n_emit, void* workspace,

@@ -30,7 +30,8 @@ def svg():
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
         ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
-         "svg_last_error", "svg_weight_sizes", "tree_accept_greedy", "tree_deltanet_commit",
+         "svg_last_error", "svg_weight_sizes", "tree_accept_greedy", "tree_accept_greedy_static",
+         "tree_deltanet_commit",
          "tree_deltanet_verify", "w4a8_linear", "w8a8_linear"])
 
 
@@ -199,6 +200,20 @@ def _tree(svg, **kw):
 def test_tree_accept_validation(svg, kw, code):
     assert _tree(svg, **kw) == code
     assert svg.last_error().startswith("tree_accept_greedy:")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=NULL), 1), (dict(parent=NULL), 1), (dict(n=NULL), 1), (dict(T=0), 1), (dict(V=0), 1),
+    (dict(T=33), 2), (dict(V=(1 << 30) + 1), 2),
+    (dict(logits=MIS), 3), (dict(emit=MIS), 3),
+])
+def test_tree_accept_static_validation(svg, kw, code):
+    # checked on the host before the library's workspace is looked up
+    args = dict(logits=A, T=4, V=100, parent=A, draft=A, target=A, path=A, emit=A, n=A)
+    args.update(kw)
+    assert svg.lib.tree_accept_greedy_static(args["logits"], args["T"], args["V"], args["parent"], args["draft"],
+                                             args["target"], args["path"], args["emit"], args["n"], NULL) == code
+    assert svg.last_error().startswith("tree_accept_greedy_static:")
 
 
 def _gdn_verify(svg, **kw):
