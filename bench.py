@@ -80,13 +80,14 @@ def weight_bytes(N, K, fmt, group):
 class Stack:
     """The synthetic stack resident on the device, and its captured passes."""
 
-    def __init__(self, workload, layers, dev, fused=True, block=32):
+    def __init__(self, workload, layers, dev, fused=True, block=32, engine="launches"):
         import torch
         import speculative_verify_gemm_amd as svg
         import synth
         self.torch, self.svg, self.synth = torch, svg, synth
         self.fused = fused
         self.block = block
+        self.engine = engine
         self.wl = workload
         self.spec = WORKLOADS[workload]
         self.fmt, self.group = self.spec["fmt"], self.spec["group"]
@@ -166,21 +167,47 @@ class Stack:
                 else:
                     self.linear(io, L, name, space)
 
+    def uses_pass(self, M):
+        """Whether the one-launch pass runs this workload at M (W4 formats with
+        groups of 64 / 128, M <= 16); otherwise one launch per linear."""
+        return (self.engine == "pass" and self.fmt != "w8" and self.group in (64, 128) and M <= 16
+                and self.fused)
+
+    def make_pass(self, io):
+        """The whole pass as one launch: every linear of every layer a step
+        that waits for all earlier steps (a decoder's linears depend on each
+        other through the ops between them)."""
+        steps = []
+        for L in range(self.layers):
+            for name, _members, N, _K, space in LAYER_LAUNCHES:
+                wq, ws, wz, _n = self.w[L][name]
+                steps.append(dict(X=io["xin"][L][space], signs=self.signs[L][space], xq=io["xq"][space],
+                                  x_scale=io["xs"][space], wq=wq, w_scale=ws, w_zero=wz, N=N,
+                                  y=io["ys"][L][name], after=1))
+        return self.svg.LinearPass(steps, self.fmt, self.group, block=self.block)
+
     def pass_bytes(self, M):
         return sum(linear_bytes(M, N, K, self.fmt, self.group) for _n, _m, N, K, _s in LAYER_LAUNCHES) * self.layers
 
     def capture(self, io):
         torch = self.torch
+        if self.uses_pass(io["M"]):
+            io["pass"] = self.make_pass(io)
+            step = io["pass"].run
+        else:
+            step = lambda: self.run_pass(io)  # noqa: E731
         s = torch.cuda.Stream(self.dev)
         s.wait_stream(torch.cuda.current_stream(self.dev))
         with torch.cuda.stream(s):
-            self.run_pass(io)  # warm the launch path outside capture
+            step()  # warm the launch path outside capture
         torch.cuda.current_stream(self.dev).wait_stream(s)
         torch.cuda.synchronize(self.dev)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.run_pass(io)
+            step()
         torch.cuda.synchronize(self.dev)
+        if "pass" in io and io["pass"].gave_up():
+            raise RuntimeError("the one-launch pass gave up a wait: its timings would be meaningless")
         return g
 
 

@@ -330,6 +330,73 @@ svg_status tree_deltanet_commit(float* state, const float* k, const float* v, co
                                 const float* beta, const int32_t* path, const int32_t* n_emit, int T,
                                 int H, int dk, int dv, void* stream);
 
+/*
+ * One pass of dependent W4A8 linears in ONE persistent launch.
+ * [KT "Why batch-one decoding is memory-bound": a pass streams every weight
+ *  once, so its time is bytes / bandwidth only if the weight stream never
+ *  pauses; "How Uzu optimizes bytes and tokens per pass": activations are
+ *  rotated and quantized on the fly; "Producing several tokens from one model
+ *  pass": the verify pass runs the same linears on 16-32 candidate rows.]
+ *
+ * A pass is a list of steps, each act_quant_w4a8_linear on its own fp32 input
+ * rows X (M rows, shared M).  With `after` set, a step's X is read only once
+ * every earlier step has finished and its y is visible device-wide (y may be,
+ * or feed, a later step's X); the launch keeps the weight stream going across
+ * those waits by loading later steps' weights (which depend on nothing) ahead
+ * of the activations.  Results are bit-identical in xq / x_scale / partials
+ * to the single calls, and y agrees within fp32 summation order.
+ *
+ *  svg_pass_step   X, signs, xq, x_scale, wq, w_scale, w_zero, y,
+ *                  partials_debug as for act_quant_w4a8_linear (same layouts,
+ *                  same alignment); N >= 1 rows; K with K % 32 == 0,
+ *                  K % group == 0, K % block == 0, K <= 12288; after: 0 or 1.
+ *  svg_pass_plan   validates every step on the host and writes the pass's
+ *                  device image to plan_host (host memory, info->plan_bytes;
+ *                  NULL: validate and size only); the caller copies it to
+ *                  device memory (8-byte aligned) once and may run it any
+ *                  number of times.  All steps share M (1..16), fmt
+ *                  (SVG_W4_ASYM_Z4 or _Z16), group (64 or 128) and block.
+ *                  Fills *info (sizes included).
+ *  svg_pass_run    enqueues the pass: one launch of one 1024-thread
+ *                  workgroup per compute unit.  plan: the uploaded image;
+ *                  info: as filled by svg_pass_plan; workspace:
+ *                  info->workspace_bytes of device memory, 256-byte aligned,
+ *                  zero-filled before first use; each run leaves its counters
+ *                  zero-filled again, so it is reused as it is.  Word 0 is a
+ *                  sticky flag the launch sets (to 1) if one of its bounded
+ *                  waits ever gave up (then the outputs are undefined); it
+ *                  needs every workgroup resident at once, i.e. no other
+ *                  work on the device while it runs.  Runs that may overlap
+ *                  need different workspaces.  The step table's pointers are
+ *                  baked into the image: buffers must stay where they were.
+ *  Errors: SVG_EINVAL / SVG_EUNSUPPORTED / SVG_EALIGN as for the single
+ *  calls, plus SVG_EUNSUPPORTED for nsteps < 1, M > 16, group 32, K > 12288
+ *  or a device with fewer than 8 compute units; svg_pass_run checks info
+ *  against its own limits only (the image is trusted).
+ */
+typedef struct svg_pass_step {
+    const float* X;
+    const int8_t* signs;
+    int8_t* xq;
+    float* x_scale;
+    const uint8_t* wq;
+    const uint16_t* w_scale;
+    const void* w_zero;
+    float* y;
+    int32_t* partials_debug;
+    int N, K;
+    int after;
+} svg_pass_step;
+
+typedef struct svg_pass_info {
+    int nsteps, M, fmt, group, block;
+    uint64_t plan_bytes, workspace_bytes;
+} svg_pass_info;
+
+svg_status svg_pass_plan(const svg_pass_step* steps, int nsteps, int M, int fmt, int group, int block,
+                         void* plan_host, uint64_t plan_host_bytes, svg_pass_info* info);
+svg_status svg_pass_run(const void* plan, const svg_pass_info* info, void* workspace, void* stream);
+
 /* Text of the last error on the calling thread ("" after a successful call);
  * valid until the next call on this thread. */
 const char* svg_last_error(void);

@@ -52,6 +52,10 @@ def _load():
                lib.tree_accept_greedy_static,
                lib.tree_deltanet_verify, lib.tree_deltanet_commit):
         fn.restype = ctypes.c_int
+    lib.svg_pass_plan.argtypes = [vp, i, i, i, i, i, vp, ctypes.c_uint64, vp]
+    lib.svg_pass_run.argtypes = [vp, vp, vp, vp]
+    lib.svg_pass_plan.restype = ctypes.c_int
+    lib.svg_pass_run.restype = ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.svg_weight_sizes.argtypes = [i, i, i, i, u64p, u64p, u64p]
     lib.svg_weight_sizes.restype = ctypes.c_int
@@ -346,3 +350,78 @@ def stacked_slices(wq, w_scale, w_zero, rows_before, N, K, fmt, group):
         return wq[w0:w0 + w1], w_scale[rows_before:rows_before + N], None
     es = w_zero.element_size()
     return (wq[w0:w0 + w1], w_scale[s0 // 2:(s0 + s1) // 2], w_zero[z0 // es:(z0 + z1) // es])
+
+
+# ------------------------------------------------------------ one-launch pass
+class PassStepC(ctypes.Structure):
+    """svg_pass_step (include/svgemm.h)."""
+    _fields_ = [("X", ctypes.c_void_p), ("signs", ctypes.c_void_p), ("xq", ctypes.c_void_p),
+                ("x_scale", ctypes.c_void_p), ("wq", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("w_zero", ctypes.c_void_p), ("y", ctypes.c_void_p), ("partials_debug", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("K", ctypes.c_int), ("after", ctypes.c_int)]
+
+
+class PassInfoC(ctypes.Structure):
+    """svg_pass_info (include/svgemm.h)."""
+    _fields_ = [("nsteps", ctypes.c_int), ("M", ctypes.c_int), ("fmt", ctypes.c_int), ("group", ctypes.c_int),
+                ("block", ctypes.c_int), ("plan_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+
+class LinearPass:
+    """A pass of dependent W4A8 linears run as ONE launch (svg_pass_plan /
+    svg_pass_run).  `steps`: dicts with X [M, K] fp32, signs [K] int8, xq
+    [M, K] int8 and x_scale [M] fp32 (outputs), wq / w_scale / w_zero (the
+    tiled storage), N, y [M, N] fp32, optional partials_debug [M, N, K/group]
+    int32, and `after` (read X only once every earlier step has finished).
+    The plan image is uploaded once; the tensors must stay alive and in place
+    (the object keeps references)."""
+
+    def __init__(self, steps, fmt, group, block=BLOCK, device=None):
+        if not steps:
+            raise ValueError("a pass needs at least one step")
+        f = _fmt(fmt)
+        M = steps[0]["X"].shape[0]
+        arr = (PassStepC * len(steps))()
+        self._keep = []
+        for i, st in enumerate(steps):
+            X, sg, xq, xs, y = st["X"], st["signs"], st["xq"], st["x_scale"], st["y"]
+            _dev(X, "X", torch.float32)
+            _dev(sg, "signs", torch.int8)
+            _dev(xq, "xq", torch.int8)
+            _dev(xs, "x_scale", torch.float32)
+            _dev(y, "y", torch.float32)
+            m, K = X.shape
+            N = int(st["N"])
+            if m != M:
+                raise ValueError("every step of a pass has the same M")
+            if tuple(xq.shape) != (M, K) or tuple(xs.shape) != (M,) or tuple(y.shape) != (M, N):
+                raise ValueError("step shapes: xq [M, K], x_scale [M], y [M, N]")
+            _check_storage(N, K, f, group, st["wq"], st["w_scale"], st["w_zero"])
+            dbg = st.get("partials_debug")
+            if dbg is not None:
+                _dev(dbg, "partials_debug", torch.int32)
+                if tuple(dbg.shape) != (M, N, K // group):
+                    raise ValueError("partials_debug must be [M, N, K/g]")
+            arr[i] = PassStepC(X.data_ptr(), sg.data_ptr(), xq.data_ptr(), xs.data_ptr(), st["wq"].data_ptr(),
+                               st["w_scale"].data_ptr(), st["w_zero"].data_ptr(), y.data_ptr(),
+                               dbg.data_ptr() if dbg is not None else None, N, K, int(st.get("after", 1)))
+            self._keep.append(st)
+        self.info = PassInfoC()
+        _check(lib.svg_pass_plan(arr, len(steps), M, f, group, block, None, 0, ctypes.byref(self.info)))
+        host = ctypes.create_string_buffer(self.info.plan_bytes)
+        _check(lib.svg_pass_plan(arr, len(steps), M, f, group, block, host, self.info.plan_bytes,
+                                 ctypes.byref(self.info)))
+        dev = device if device is not None else steps[0]["X"].device
+        self.plan = torch.frombuffer(bytearray(host.raw), dtype=torch.uint8).to(dev)
+        self.workspace = torch.zeros(self.info.workspace_bytes, dtype=torch.uint8, device=dev)
+        if self.workspace.data_ptr() % 256 or self.plan.data_ptr() % 8:
+            raise RuntimeError("device allocations are not aligned as the pass needs")
+
+    def run(self, stream=None):
+        _check(lib.svg_pass_run(_p(self.plan), ctypes.byref(self.info), _p(self.workspace),
+                                _stream(stream, self.plan)))
+
+    def gave_up(self) -> bool:
+        """Whether a run of this pass ever gave up a bounded wait (word 0 of
+        its workspace; its outputs are then undefined)."""
+        return bool(int(self.workspace[:4].view(torch.int32).cpu()[0]))

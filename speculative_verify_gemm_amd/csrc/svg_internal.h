@@ -44,6 +44,16 @@ hipError_t svg_launch_gdn_tree_commit(float* state, const float* k, const float*
                                       const float* beta, const int32_t* path, const int32_t* n_emit, int T, int H,
                                       int dk, int dv, hipStream_t stream);
 
+// One pass of dependent W4A8 linears in one launch (pass.hip).  check:
+// validates the steps, sizes the plan image and the workspace; returns an
+// error text (and the status in *code) or nullptr.  write: the plan image into
+// host memory.  launch: one persistent launch of the uploaded image.
+struct svg_pass_step;
+const char* svg_pass_check(const svg_pass_step* steps, int nsteps, int M, int fmt, int group, int block,
+                           uint64_t* plan_bytes, uint64_t* ws_bytes, int* code);
+void svg_pass_write(const svg_pass_step* steps, int nsteps, int M, int fmt, int group, int block, void* plan_host);
+hipError_t svg_launch_pass(const void* plan, int M, int fmt, int group, void* ws, hipStream_t stream);
+
 // Bytes of the weight storage (include/svgemm.h describes the layout).
 // W4 codes: tiled, rows padded to 16 and K to 128.  Scales and zeros:
 // blocked per (16-row tile, 512-k block, row), rows padded to 16 and K to

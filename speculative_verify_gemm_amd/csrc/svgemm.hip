@@ -292,6 +292,43 @@ svg_status tree_accept_greedy_static(const float* logits, int T, int V, const in
   return hip_status(fn, svg_launch_tree_accept(logits, T, V, parent, draft, target, path, emit, n_emit, ws, s));
 }
 
+svg_status svg_pass_plan(const svg_pass_step* steps, int nsteps, int M, int fmt, int group, int block,
+                         void* plan_host, uint64_t plan_host_bytes, svg_pass_info* info) {
+  static const char* fn = "svg_pass_plan";
+  if (!info) return fail(SVG_EINVAL, fn, "null info");
+  uint64_t pb = 0, wb = 0;
+  int code = SVG_OK;
+  const char* err = svg_pass_check(steps, nsteps, M, fmt, group, block, &pb, &wb, &code);
+  if (err) return fail(code, fn, err);
+  if (plan_host) {
+    if (plan_host_bytes < pb) return fail(SVG_EINVAL, fn, "plan_host is smaller than info->plan_bytes");
+    if (!aligned(plan_host, 8)) return fail(SVG_EALIGN, fn, "plan_host needs 8-byte alignment");
+    svg_pass_write(steps, nsteps, M, fmt, group, block, plan_host);
+  }
+  info->nsteps = nsteps;
+  info->M = M;
+  info->fmt = fmt;
+  info->group = group;
+  info->block = block;
+  info->plan_bytes = pb;
+  info->workspace_bytes = wb;
+  return ok();
+}
+
+svg_status svg_pass_run(const void* plan, const svg_pass_info* info, void* workspace, void* stream) {
+  static const char* fn = "svg_pass_run";
+  if (!plan || !info || !workspace) return fail(SVG_EINVAL, fn, "null pointer");
+  if (info->nsteps < 1 || info->M < 1) return fail(SVG_EINVAL, fn, "info has nsteps < 1 or M < 1");
+  if (info->M > 16 || (info->fmt != SVG_W4_ASYM_Z4 && info->fmt != SVG_W4_ASYM_Z16) ||
+      (info->group != 64 && info->group != 128) || (info->block != 32 && info->block != 64))
+    return fail(SVG_EUNSUPPORTED, fn, "info names an unsupported M, fmt, group or block");
+  if (!aligned(plan, 8)) return fail(SVG_EALIGN, fn, "plan needs 8-byte alignment");
+  if (!aligned(workspace, 256)) return fail(SVG_EALIGN, fn, "workspace needs 256-byte alignment");
+  if (svg_cu_count() < 8) return fail(SVG_EUNSUPPORTED, fn, "the device has fewer than 8 compute units");
+  return hip_status(fn, svg_launch_pass(plan, info->M, info->fmt, info->group, workspace,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 svg_status tree_deltanet_verify(const float* state, const float* q, const float* k, const float* v,
                                 const float* alpha, const float* beta, const int32_t* parent, int T, int H,
                                 int dk, int dv, float* out, void* stream) {

@@ -30,7 +30,7 @@ def svg():
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
         ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
-         "svg_last_error", "svg_weight_sizes", "tree_accept_greedy", "tree_accept_greedy_static",
+         "svg_last_error", "svg_pass_plan", "svg_pass_run", "svg_weight_sizes", "tree_accept_greedy", "tree_accept_greedy_static",
          "tree_deltanet_commit",
          "tree_deltanet_verify", "w4a8_linear", "w8a8_linear"])
 
@@ -257,3 +257,74 @@ def test_size_limits_are_refused(svg):
     assert _w4(svg, N=1 << 21, K=8192, g=64) == 2                                     # 8 GiB of codes
     assert svg.lib.rht_rotate_weights(A, 1 << 21, 8192, A, 32, 1, 64, A, A, A, NULL, NULL) == 2
     assert _tree(svg, V=(1 << 30) + 1) == 2
+
+
+# ------------------------------------------------------------ one-launch pass
+def _pass_steps(svg, n=2, **kw):
+    arr = (svg.PassStepC * n)()
+    for i in range(n):
+        d = dict(X=0x10000, signs=0x10000, xq=0x10000, x_scale=0x10000, wq=0x10000, w_scale=0x10000,
+                 w_zero=0x10000, y=0x10000, partials_debug=None, N=64, K=4096, after=1)
+        d.update(kw if i == n - 1 else {})
+        arr[i] = svg.PassStepC(**d)
+    return arr
+
+
+def _plan(svg, steps, n=2, M=16, fmt=1, g=64, block=32):
+    info = svg.PassInfoC()
+    st = svg.lib.svg_pass_plan(steps, n, M, fmt, g, block, None, 0, ctypes.byref(info))
+    return st, info
+
+
+def test_pass_plan_sizes_the_plan_and_workspace(svg):
+    st, info = _plan(svg, _pass_steps(svg))
+    assert st == 0 and info.nsteps == 2 and info.M == 16
+    assert info.plan_bytes == 64 + 2 * 136
+    # counters, the per-XCC staging rows (M >= 2) and the two halves' partials of
+    # each K = 4096 step (none: 16 x 4096 fits LDS)
+    assert info.workspace_bytes % 256 == 0 and info.workspace_bytes > 8 * 16 * 12288
+    st1, info1 = _plan(svg, _pass_steps(svg), M=1)
+    assert st1 == 0 and info1.workspace_bytes < 64 * 1024       # no staging at M = 1
+    # a K = 12288 step at M = 16 is cut in two halves: 4 tiles x 2 x 256 fp32 partials more
+    st2, info2 = _plan(svg, _pass_steps(svg, K=12288))
+    assert st2 == 0 and info2.workspace_bytes >= info.workspace_bytes + 4 * 2 * 256 * 4
+
+
+def test_pass_plan_writes_the_image(svg):
+    steps = _pass_steps(svg)
+    st, info = _plan(svg, steps)
+    buf = ctypes.create_string_buffer(info.plan_bytes)
+    assert svg.lib.svg_pass_plan(steps, 2, 16, 1, 64, 32, buf, info.plan_bytes, ctypes.byref(info)) == 0
+    raw = bytes(buf.raw)
+    assert int.from_bytes(raw[:4], "little") == 0x53564750 and int.from_bytes(raw[4:8], "little") == 2
+    small = ctypes.create_string_buffer(info.plan_bytes - 8)
+    assert svg.lib.svg_pass_plan(steps, 2, 16, 1, 64, 32, small, info.plan_bytes - 8, ctypes.byref(info)) == 1
+
+
+@pytest.mark.parametrize("kw,args,code", [
+    (dict(X=None), {}, 1), (dict(y=None), {}, 1), (dict(w_zero=None), {}, 1), (dict(N=0), {}, 1),
+    (dict(after=2), {}, 1),
+    ({}, dict(M=17), 2), ({}, dict(g=32), 2), ({}, dict(fmt=2), 2), ({}, dict(block=16), 2),
+    (dict(K=12416), {}, 2), (dict(K=4000), {}, 2), (dict(K=4160), dict(g=128), 2),
+    (dict(X=0x10004), {}, 3), (dict(wq=0x10008), {}, 3), (dict(y=0x10002), {}, 3),
+])
+def test_pass_plan_validation(svg, kw, args, code):
+    st, _info = _plan(svg, _pass_steps(svg, **kw), **args)
+    assert st == code
+    assert svg.last_error().startswith("svg_pass_plan:")
+
+
+def test_pass_plan_needs_steps(svg):
+    info = svg.PassInfoC()
+    assert svg.lib.svg_pass_plan(None, 1, 1, 1, 64, 32, None, 0, ctypes.byref(info)) == 1
+    assert svg.lib.svg_pass_plan(_pass_steps(svg), 0, 1, 1, 64, 32, None, 0, ctypes.byref(info)) == 2
+
+
+def test_pass_run_validation(svg):
+    st, info = _plan(svg, _pass_steps(svg))
+    assert st == 0
+    assert svg.lib.svg_pass_run(None, ctypes.byref(info), A, NULL) == 1
+    assert svg.lib.svg_pass_run(A, ctypes.byref(info), None, NULL) == 1
+    assert svg.lib.svg_pass_run(A, ctypes.byref(info), ctypes.c_void_p(0x10080), NULL) == 3   # not 256-aligned
+    bad = svg.PassInfoC(2, 17, 1, 64, 32, info.plan_bytes, info.workspace_bytes)
+    assert svg.lib.svg_pass_run(A, ctypes.byref(bad), A, NULL) == 2
