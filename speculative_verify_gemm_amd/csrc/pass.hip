@@ -143,11 +143,41 @@ SVG_DEV bool poll_ge(const u32* p, u32 target, u32* ws) {
   return true;
 }
 
+// Stores through global-address-space pointers: a store through a generic
+// pointer is a FLAT operation, which the compiler must assume may complete out
+// of order with the weight loads -- every later wait on the ring would then
+// drain it whole.
+typedef __attribute__((address_space(1))) u32 global_u32;
+typedef __attribute__((address_space(1))) int32_t global_i32;
+SVG_DEV void gstore(u32* p, u32 v) { *(global_u32*)p = v; }
+SVG_DEV void gstore(int32_t* p, int32_t v) { *(global_i32*)p = v; }
+SVG_DEV void gstore(float* p, float v) { gstore(reinterpret_cast<u32*>(p), __float_as_uint(v)); }
+typedef __attribute__((address_space(1))) float global_f32;
+// An agent-scope store / load of a float through the global address space.
+SVG_DEV void gstore_dev(float* p, float v) {
+  __hip_atomic_store((global_f32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SVG_DEV float gload_dev(const float* p) {
+  return __hip_atomic_load((const global_f32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Phase timestamps (the 100 MHz real-time counter) for tracing a run: slot
 // p of (step j, workgroup); a no-op unless the plan carries a trace buffer.
 constexpr int kTracePhases = 8;
 SVG_DEV void trace_at(u32* trace, int j, int p) {
-  if (trace) trace[((size_t)j * gridDim.x + blockIdx.x) * kTracePhases + p] = (u32)__builtin_amdgcn_s_memrealtime();
+  if (trace) gstore(trace + ((size_t)j * gridDim.x + blockIdx.x) * kTracePhases + p, (u32)__builtin_amdgcn_s_memrealtime());
+}
+
+// A value the same on every lane of the wave, said so to the compiler (its
+// uniformity analysis cannot see through the spin loops on LDS counts in the
+// stream waves' loop; state it thinks divergent would live in vector
+// registers and cost a vector instruction per scalar one).
+SVG_DEV int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+SVG_DEV u32 uni(u32 v) { return (u32)__builtin_amdgcn_readfirstlane((int)v); }
+template <typename T>
+SVG_DEV T* uni(T* p) {
+  const uint64_t a = (uint64_t)p;
+  return (T*)(((uint64_t)uni((u32)(a >> 32)) << 32) | uni((u32)a));
 }
 
 SVG_DEV u32 hw_xcc() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 7u; }
@@ -163,36 +193,40 @@ SVG_DEV bool arrive(u32* ws, int j, int nsteps) {
 }
 
 // ---------------------------------------------------------------- geometry
-// One step as one workgroup (and one stream wave) sees it.
+// One step as one workgroup (and one stream wave) sees it.  Every workgroup
+// walks the same number of tile slots in a step, ceil(tiles / workgroups per
+// half of K); a slot past the last tile is walked without touching memory.
+// So the walk is counters only, with no search for the next step a
+// workgroup has work in (a loop between the weight loads and their use would
+// hide from the compiler how many loads are still in flight).
 struct Geo {
-  int ntw, t0, ts;       // tiles of this workgroup: t0, t0 + ts, ...
-  int jb, je, jrel0;     // this wave's chunks [jb, je); first chunk of the LDS rows
+  int nts, t0, ts;       // tile slots: tiles t0, t0 + ts, ... (nts of them)
+  int jrel0, len;        // the workgroup's chunks of K: [jrel0, jrel0 + len), the first held by the LDS rows
   int h;                 // split steps: the half of K this workgroup takes
+  int tlim;              // tiles below tlim are real (0: none for this workgroup)
 };
 
-SVG_DEV Geo step_geo(const PassStep& S, int swave) {
+SVG_DEV Geo step_geo(const PassStep& S) {
   Geo g;
   const int G = gridDim.x, bid = blockIdx.x;
-  int base, len;
   if (S.split) {
     const int G2 = G / 2, p = bid >> 1;
     g.h = bid & 1;
     g.t0 = p;
     g.ts = G2;
-    g.ntw = (p < G2 && p < S.ntiles) ? (S.ntiles - 1 - p) / G2 + 1 : 0;
-    base = g.h * S.KH;
-    len = min(S.KH, S.KT - base);
+    g.nts = (S.ntiles + G2 - 1) / G2;
+    g.tlim = p < G2 ? S.ntiles : 0;  // an odd workgroup out has no pair
+    g.jrel0 = g.h * S.KH;
+    g.len = min(S.KH, S.KT - g.jrel0);
   } else {
     g.h = 0;
     g.t0 = bid;
     g.ts = G;
-    g.ntw = bid < S.ntiles ? (S.ntiles - 1 - bid) / G + 1 : 0;
-    base = 0;
-    len = S.KT;
+    g.nts = (S.ntiles + G - 1) / G;
+    g.tlim = S.ntiles;
+    g.jrel0 = 0;
+    g.len = S.KT;
   }
-  g.jrel0 = base;
-  g.jb = base + swave * S.cpw;
-  g.je = min(base + len, g.jb + S.cpw);
   return g;
 }
 
@@ -207,106 +241,213 @@ SVG_DEV bool waits(const PassStep& S, int j, int M) { return j > 0 && (S.after |
 SVG_DEV int rows_of(int rank, int nx, int M) { return rank < M ? (M - 1 - rank) / nx + 1 : 0; }
 
 // ------------------------------------------------------------- stream side
-// A stream wave's position in its chunk sequence: step j (nsteps: past the
-// end), tile ordinal ti, chunk ordinal c within the wave's range.
-struct Walk {
-  const PassStep* plan;
-  int nsteps, swave;
-  int j, ti, c;
-  Geo g;
-  int cpw;
+// A stream wave's share of a step: in every tile slot, chunks [jb, jb + cw)
+// of the tile (absolute chunk indices along K).  The workgroup's range of K
+// (all of it, or one half) is cut among the 12 waves into runs that differ by
+// at most one chunk, so no wave walks a chunk outside the matrix.  A wave left
+// without chunks (K under 12 chunks) walks one chunk per tile slot through a
+// resource of no bytes: zeros, no memory traffic.
+SVG_DEV void wave_share(const Geo& g, int swave, int& jb, int& cw, bool& real) {
+  const int q = g.len / kStreamWaves, rem = g.len % kStreamWaves;
+  cw = q + (swave < rem ? 1 : 0);
+  jb = g.jrel0 + swave * q + min(swave, rem);
+  real = cw > 0;
+  if (!real) {
+    cw = 1;
+    jb = g.jrel0;
+  }
+}
 
-  // Move to the first chunk of the first step from `from` on where this
-  // workgroup has tiles; returns that step (or null past the end).
-  SVG_DEV const PassStep* enter(int from) {
-    ti = c = 0;
-    cpw = 1;
-    g = Geo{0, 0, 1, 0, 0, 0, 0};
-    for (j = from; j < nsteps; ++j) {
-      const PassStep* S = plan + j;
-      g = step_geo(*S, swave);
-      if (g.ntw == 0) continue;
-      cpw = S->cpw;
-      return S;
+// The position of a stream wave's walk: step j (nsteps: past the end), tile
+// slot ti of nts (tile t, stride ts; tiles from tlim on are not real), the
+// wave's run of cw chunks from jb, and `left` chunks of the current slot still
+// to go.  The walk is counters only (no search for the next step a workgroup
+// has work in: a loop between the weight loads and their use would hide from
+// the compiler how many loads are still in flight).
+struct WalkPos {
+  int j, ti, nts, t, ts, tlim;
+  int jb, cw, left;
+  bool real;
+  // The current step's table entry, addressed through a uniform index so
+  // that it is read with scalar loads (a vector load would be a memory
+  // operation of unknown count in the stream waves' loop).
+  SVG_DEV const PassStep* step(const PassStep* plan) const { return plan + __builtin_amdgcn_readfirstlane(j); }
+  // Enter step `to`; false past the end, where the walk stays (`left` never
+  // runs out again).  Every field is written on both paths, after the branch
+  // (stores to different fields at the end of two branches get merged into
+  // one store at a computed address, and then the whole stream context stays
+  // in scratch memory).
+  SVG_DEV bool enter(const PassStep* plan, int nsteps, int swave, int to) {
+    const bool ok = to < nsteps;
+    int nts_ = 0, t_ = 0, ts_ = 0, tlim_ = 0, jb_ = 0, cw_ = 0, left_ = 1 << 30;
+    bool real_ = false;
+    if (ok) {
+      const Geo g = step_geo(plan[uni(to)]);
+      nts_ = g.nts;
+      t_ = g.t0;
+      ts_ = g.ts;
+      tlim_ = g.tlim;
+      wave_share(g, swave, jb_, cw_, real_);
+      left_ = cw_;
     }
-    return nullptr;
+    j = to;
+    ti = 0;
+    nts = nts_;
+    t = t_;
+    ts = ts_;
+    tlim = tlim_;
+    jb = jb_;
+    cw = cw_;
+    left = left_;
+    real = real_;
+    return ok;
   }
-  // Next chunk; returns the new step when the walk entered one, else null.
-  SVG_DEV const PassStep* advance() {
-    if (++c < cpw) return nullptr;
-    c = 0;
-    if (++ti < g.ntw) return nullptr;
-    return enter(j + 1);
+  // After the last chunk of a tile slot: the next slot (returns 0), the next
+  // step (1) or the end (2).
+  SVG_DEV int next_tile(const PassStep* plan, int nsteps, int swave) {
+    if (++ti < nts) {
+      t += ts;
+      left = cw;
+      return 0;
+    }
+    return enter(plan, nsteps, swave, j + 1) ? 1 : 2;
   }
-  SVG_DEV bool at_end() const { return j >= nsteps; }
-  SVG_DEV int tile() const { return g.t0 + ti * g.ts; }
-  SVG_DEV int chunk() const { return g.jb + c; }
-  SVG_DEV bool valid() const { return j < nsteps && chunk() < g.je; }
+  SVG_DEV bool tile_real() const { return real && t < tlim; }
+  // Every field is the same on all lanes; say so after the walk moves.
+  SVG_DEV void uniform() {
+    j = uni(j);
+    ti = uni(ti);
+    nts = uni(nts);
+    t = uni(t);
+    ts = uni(ts);
+    tlim = uni(tlim);
+    jb = uni(jb);
+    cw = uni(cw);
+    left = uni(left);
+    real = uni((int)real) != 0;
+  }
 };
 
-// The issue side: buffer resources of the step it is in, and the loads of
-// one chunk (1 KiB of codes, this lane's 16 bytes, plus the group parameters
-// of its row).  Past the end, or past the wave's range, the offsets lie
-// outside the buffers and the loads return zeros without touching memory.
+// The issue side: the loads of one chunk (1 KiB of codes, this lane's 16
+// bytes, plus the group parameters of its row), addressed by a per-lane part
+// (voffset) and a scalar part stepped per chunk (soffset).  A tile slot that
+// is not real, and everything past the end, loads at per-lane offsets beyond
+// any buffer: zeros, no memory traffic.
 template <int G, bool Z4>
 struct Issuer {
   static constexpr int GPC = 128 / G, GPB = 4 * GPC;
-  Walk w;
+  // The slot registers keep the width of their loads (a 16-bit scale or zero,
+  // an 8-bit pair of 4-bit zeros): widened where the chunk is computed, not
+  // where it is loaded, so that no slot's load has to land early.
+  using SType = typename std::conditional<GPC == 2, u32, uint16_t>::type;
+  using ZType = typename std::conditional<Z4, uint8_t, SType>::type;
+  WalkPos p;
   int KT = 0, KB = 0;
-  // Until the walk enters a step (and for a workgroup with no tiles at all)
-  // the resources cover no bytes: every load through them returns zeros.
+  int jj = 0;                   // absolute chunk index of the next chunk
+  u32 woff = 0, svi = 0;        // its codes byte offset and parameter index (scalar parts)
+  u32 vw = kOOB, vs = kOOB, vz = kOOB;  // per-lane parts for this tile slot (beyond every buffer if not real)
   rsrc_t wr = make_rsrc(nullptr, 0u), sr = make_rsrc(nullptr, 0u), zr = make_rsrc(nullptr, 0u);
 
-  SVG_DEV void take(const PassStep* S) {
-    if (!S) return;
+  // lane16: this lane's 16 bytes of a chunk; lanep: its row's part of the
+  // parameter index (row r of the tile: r * GPB)
+  SVG_DEV void start_tile(u32 lane16, u32 lanep) {
+    jj = p.jb;
+    woff = ((u32)p.t * (u32)KT + (u32)jj) * 1024u;
+    svi = ((u32)p.t * (u32)KB + (u32)(jj >> 2)) * 16u * GPB + (u32)(jj & 3) * GPC;
+    const bool on = p.tile_real();
+    vw = on ? lane16 : kOOB;
+    vs = on ? lanep * 2u : kOOB;
+    vz = on ? (Z4 ? lanep >> 1 : lanep * 2u) : kOOB;
+  }
+  // After entering a step (or the end)
+  SVG_DEV void take(const PassStep* plan, bool entered, u32 lane16, u32 lanep) {
+    if (!entered) {
+      vw = vs = vz = kOOB;
+      return;
+    }
+    const PassStep* S = p.step(plan);
     KT = S->KT;
     KB = S->KB;
     wr = make_rsrc(S->wq, S->wbytes);
     sr = make_rsrc(S->ws, S->sbytes);
     zr = make_rsrc(S->wz, S->zbytes);
+    start_tile(lane16, lanep);
   }
-  SVG_DEV void next() { take(w.advance()); }
-  // z: the raw zero bytes (4-bit zeros: the byte holding the chunk's nibbles)
-  SVG_DEV void issue(u32x4& wv, u32& s, u32& z, u32 lane16, int r) const {
-    const bool v = w.valid();
-    const int t = w.tile(), jj = w.chunk();
-    wv = bload16_nt(wr, v ? ((u32)t * (u32)KT + (u32)jj) * 1024u + lane16 : kOOB);
-    const u32 vi = (((u32)t * (u32)KB + (u32)(jj >> 2)) * 16u + (u32)r) * GPB + (u32)(jj & 3) * GPC;
+  SVG_DEV void issue(u32x4& wv, SType& s, ZType& z) const {
+    wv = __builtin_amdgcn_raw_buffer_load_b128(wr, vw, woff, kNT);
     if constexpr (GPC == 2) {
-      s = bload4(sr, v ? vi * 2u : kOOB);
-      z = Z4 ? (u32)bload1(zr, v ? vi >> 1 : kOOB) : bload4(zr, v ? vi * 2u : kOOB);
+      s = __builtin_amdgcn_raw_buffer_load_b32(sr, vs, svi * 2u, 0);
+      if constexpr (Z4) z = __builtin_amdgcn_raw_buffer_load_b8(zr, vz, svi >> 1, 0);
+      else z = __builtin_amdgcn_raw_buffer_load_b32(zr, vz, svi * 2u, 0);
     } else {
-      s = bload2(sr, v ? vi * 2u : kOOB);
-      z = Z4 ? (u32)bload1(zr, v ? vi >> 1 : kOOB) : (u32)bload2(zr, v ? vi * 2u : kOOB);
+      s = __builtin_amdgcn_raw_buffer_load_b16(sr, vs, svi * 2u, 0);
+      if constexpr (Z4) z = __builtin_amdgcn_raw_buffer_load_b8(zr, vz, svi >> 1, 0);
+      else z = __builtin_amdgcn_raw_buffer_load_b16(zr, vz, svi * 2u, 0);
+    }
+  }
+  SVG_DEV void uniform() {
+    p.uniform();
+    KT = uni(KT);
+    KB = uni(KB);
+    jj = uni(jj);
+    woff = uni(woff);
+    svi = uni(svi);
+  }
+  // Step to the next chunk: the next 1 KiB of codes; the parameters of the
+  // next chunk of the 512-k block, or of the next block's first chunk.
+  SVG_DEV void advance(const PassStep* plan, int nsteps, int swave, u32 lane16, u32 lanep) {
+    woff += 1024u;
+    svi += (jj & 3) == 3 ? (u32)(16 * GPB - 3 * GPC) : (u32)GPC;
+    ++jj;
+    if (--p.left == 0) {
+      const int n = p.next_tile(plan, nsteps, swave);
+      p.uniform();
+      if (n == 0) start_tile(lane16, lanep);
+      else take(plan, n == 1, lane16, lanep);
     }
   }
 };
 
-// The consume side: what a chunk's computation and its tile's hand-over need.
+// The consume side: the chunk being computed and what its tile's hand-over
+// needs.
 template <int G, bool Z4>
 struct Consumer {
-  Walk w;
+  WalkPos p;
+  int jj = 0;               // absolute chunk index of the current chunk
+  int jrel0 = 0;            // first chunk of the LDS rows
   int N = 0, NG = 0, kpad = 0;
   int32_t* dbg = nullptr;
   int r = 0;
 
-  SVG_DEV void take(const PassStep* S) {
-    if (!S) return;
+  // After entering a new tile slot (entered: of a new step)
+  SVG_DEV void take(const PassStep* plan, bool entered) {
+    jj = p.jb;
+    if (!entered) return;
+    const PassStep* S = p.step(plan);
     N = S->N;
     NG = S->K / G;
     kpad = S->kpad;
     dbg = S->dbg;
+    jrel0 = S->split ? (blockIdx.x & 1) * S->KH : 0;
   }
-  SVG_DEV int tile() const { return w.tile(); }
-  SVG_DEV int chunk() const { return w.chunk(); }
-  SVG_DEV bool valid() const { return w.valid(); }
+  SVG_DEV void uniform() {
+    p.uniform();
+    jj = uni(jj);
+    jrel0 = uni(jrel0);
+    N = uni(N);
+    NG = uni(NG);
+    kpad = uni(kpad);
+    dbg = uni(dbg);
+  }
   SVG_DEV float scale(u32 s, int i) const { return half_bits_to_float((uint16_t)(i ? s >> 16 : s & 0xFFFF)); }
   // Zero of group i (0 or 1) of the chunk.  4-bit zeros of 128-wide groups:
   // the chunk's nibble is the odd one for odd chunks.
   SVG_DEV int zero(u32 z, int i) const {
-    if constexpr (Z4) return (int)((z >> (G == 128 ? 4 * (w.chunk() & 1) : 4 * i)) & 0xF);
+    if constexpr (Z4) return (int)((z >> (G == 128 ? 4 * (jj & 1) : 4 * i)) & 0xF);
     else return (int)half_bits_to_float((uint16_t)(i ? z >> 16 : z & 0xFFFF));
   }
+  // exact group sums are written for tests only, and only for real chunks
+  SVG_DEV bool dbg_on() const { return dbg != nullptr && p.tile_real(); }
 };
 
 SVG_DEV void unpack8(u32 w, u32& lo, u32& hi) {
@@ -329,8 +470,9 @@ SVG_DEV v4i as_v4i(u32x4 a) { return v4i{(int)a[0], (int)a[1], (int)a[2], (int)a
 // One chunk of the dot-product form (M = 1): lane (r, b) holds row r's two
 // 16-k runs; the activation runs come from the LDS row.
 template <int G, bool Z4>
-SVG_DEV void compute_dot(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 z, const int8_t* act, int b, float& acc) {
-  const int jrel = it.chunk() - it.w.g.jrel0;
+SVG_DEV void compute_dot(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 z, const int8_t* act, int b,
+                         float& acc) {
+  const int jrel = it.jj - it.jrel0;
   const u32x4 a1 = *reinterpret_cast<const u32x4*>(act + jrel * 128 + 16 * b);
   const u32x4 a2 = *reinterpret_cast<const u32x4*>(act + jrel * 128 + 64 + 16 * b);
   u32 wl[8];
@@ -351,19 +493,19 @@ SVG_DEV void compute_dot(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 z
   int S2 = p2 - it.zero(z, two ? 1 : 0) * q2;
   acc = fmaf(it.scale(s, 0), (float)S1, acc);
   acc = fmaf(it.scale(s, two ? 1 : 0), (float)S2, acc);
-  if (it.dbg != nullptr) {  // exact group sums for tests: add up the 4 lanes of each run
+  if (it.dbg_on()) {  // exact group sums for tests: add up the 4 lanes of each run
     if constexpr (!two) S1 += S2;
     S1 += lane_xor16(S1);
     S1 += lane_xor32(S1);
     S2 += lane_xor16(S2);
     S2 += lane_xor32(S2);
-    const int n = it.tile() * 16 + it.r, jj = it.chunk();
-    if (b == 0 && n < it.N && it.valid()) {
+    const int n = it.p.t * 16 + it.r, jj = it.jj;
+    if (b == 0 && n < it.N) {
       if (two) {
-        if (2 * jj < it.NG) it.dbg[(size_t)n * it.NG + 2 * jj] = S1;
-        if (2 * jj + 1 < it.NG) it.dbg[(size_t)n * it.NG + 2 * jj + 1] = S2;
+        if (2 * jj < it.NG) gstore(it.dbg + (size_t)n * it.NG + 2 * jj, S1);
+        if (2 * jj + 1 < it.NG) gstore(it.dbg + (size_t)n * it.NG + 2 * jj + 1, S2);
       } else if (jj < it.NG) {
-        it.dbg[(size_t)n * it.NG + jj] = S1;
+        gstore(it.dbg + (size_t)n * it.NG + jj, S1);
       }
     }
   }
@@ -375,7 +517,7 @@ SVG_DEV void compute_dot(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 z
 template <int G, bool Z4>
 SVG_DEV void compute_mfma(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 z, const int8_t* act, int M, int b,
                           float (&acc)[4]) {
-  const int jrel = it.chunk() - it.w.g.jrel0;
+  const int jrel = it.jj - it.jrel0;
   const int r = it.r;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int8_t* row = act + (r < M ? r : 0) * it.kpad + jrel * 128 + 16 * b;
@@ -395,14 +537,14 @@ SVG_DEV void compute_mfma(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 
       acc[i] = fmaf(s1, (float)e1[i], acc[i]);
       acc[i] = fmaf(s2, (float)e2[i], acc[i]);
     }
-    if (it.dbg != nullptr && it.valid()) {
-      const int n = it.tile() * 16 + r, jj = it.chunk();
+    if (it.dbg_on()) {
+      const int n = it.p.t * 16 + r, jj = it.jj;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * b + i;
         if (m < M && n < it.N) {
-          if (2 * jj < it.NG) it.dbg[((size_t)m * it.N + n) * it.NG + 2 * jj] = e1[i];
-          if (2 * jj + 1 < it.NG) it.dbg[((size_t)m * it.N + n) * it.NG + 2 * jj + 1] = e2[i];
+          if (2 * jj < it.NG) gstore(it.dbg + ((size_t)m * it.N + n) * it.NG + 2 * jj, e1[i]);
+          if (2 * jj + 1 < it.NG) gstore(it.dbg + ((size_t)m * it.N + n) * it.NG + 2 * jj + 1, e2[i]);
         }
       }
     }
@@ -411,12 +553,12 @@ SVG_DEV void compute_mfma(const Consumer<G, Z4>& it, const u32x4& w, u32 s, u32 
     const float s1 = it.scale(s, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(s1, (float)e[i], acc[i]);
-    if (it.dbg != nullptr && it.valid()) {
-      const int n = it.tile() * 16 + r, jj = it.chunk();
+    if (it.dbg_on()) {
+      const int n = it.p.t * 16 + r, jj = it.jj;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * b + i;
-        if (m < M && n < it.N && jj < it.NG) it.dbg[((size_t)m * it.N + n) * it.NG + jj] = e[i];
+        if (m < M && n < it.N && jj < it.NG) gstore(it.dbg + ((size_t)m * it.N + n) * it.NG + jj, e[i]);
       }
     }
   }
@@ -433,19 +575,24 @@ struct PassLds {
   u32 act_sync;                               // act waves' own barrier count
   int rank, nx;                               // this workgroup's rank in its XCC, XCC size
 };
+// The workgroup's LDS, named at namespace scope so that every access is known
+// to be an LDS access (through a generic pointer it would be a FLAT one, which
+// the compiler must assume completes out of order with the weight loads).
+__shared__ PassLds g_lds;
+
 SVG_DEV u32 lds_ld(const u32* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
 SVG_DEV void lds_add(u32* p, u32 v) { __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
 SVG_DEV void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// Spin until an LDS count reaches target; bounded like every other wait.
-SVG_DEV void lds_wait_ge(const u32* p, u32 target, u32* ws) {
+// Spin until an LDS count reaches target; bounded like every other wait
+// (true if it gave up).  The loop touches LDS only: a global access in a loop
+// of the stream waves would hide from the compiler how many of their weight
+// loads are still in flight, and every later wait would drain them all.
+SVG_DEV bool lds_wait_ge(const u32* p, u32 target) {
   for (u32 it = 0; lds_ld(p) < target; ++it) {
-    if ((it & 4095u) == 4095u && __hip_atomic_load(ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
-    if (it > (1u << 23)) {
-      __hip_atomic_store(ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
+    if (it > (1u << 23)) return true;
     __builtin_amdgcn_s_sleep(1);
   }
+  return false;
 }
 
 // A barrier of the four act waves alone (the stream waves go on): an LDS
@@ -458,7 +605,7 @@ struct ActSync {
     lds_fence();
     if (lane == 0) lds_add(count, 1u);
     ++phase;
-    lds_wait_ge(count, 4u * phase, ws);
+    if (lds_wait_ge(count, 4u * phase)) st_dev(ws, 1u);
     asm volatile("" ::: "memory");
   }
 };
@@ -518,18 +665,19 @@ SVG_DEV void act_quant_m1(const PassStep& S, PassLds& L, int atid, int awave, Ac
   const float wmax = quant_row_regs<CPT, B>(S.X, S.K, S.signs, e, atid);
   if ((atid & 63) == 0) L.red[awave] = wmax;
   sync(atid & 63);
+
   const float amax = fmaxf(fmaxf(L.red[0], L.red[1]), fmaxf(L.red[2], L.red[3]));
   const bool out = blockIdx.x == 0;
   u32* xq = reinterpret_cast<u32*>(S.xq);
   codes_of_row<CPT>(e, S.K, amax, atid, [&](u32 c, u32 v) {
     L.act[c] = v;
-    if (out) xq[c] = v;
+    if (out) gstore(xq + c, v);
   });
   for (int wd = S.K / 4 + atid; wd < S.kpad / 4; wd += kActThreads) L.act[wd] = 0u;  // zero past K
   if (atid == 0) {
     const float sc = (amax / 127.0f) * (1.0f / B);
     L.xs[0] = sc;
-    if (out) *S.x_scale = sc;
+    if (out) gstore(S.x_scale, sc);
   }
   wg_barrier();
 }
@@ -571,13 +719,13 @@ SVG_DEV void act_quant_row_stage(const PassStep& S, PassLds& L, int m, int M, u3
     int q[4] = {0, 0, 0, 0};
     if (amax > 0.f) act_codes4(u, sigma, rinv, fast, q);
     const u32 v = pack4(q);
-    stage[c] = v;
-    if (out) xq[(((u32)c >> 3) * (u32)M + (u32)m) * 8u + ((u32)c & 7u)] = v;
+    gstore(stage + c, v);
+    if (out) gstore(xq + (((u32)c >> 3) * (u32)M + (u32)m) * 8u + ((u32)c & 7u), v);
   }
   if (atid == 0) {
     const float sc = sigma * (1.0f / B);
-    reinterpret_cast<float*>(ws + H.sbase + xcc * kLine)[m] = sc;
-    if (out) S.x_scale[m] = sc;
+    gstore(reinterpret_cast<float*>(ws + H.sbase + xcc * kLine) + m, sc);
+    if (out) gstore(S.x_scale + m, sc);
   }
   wait_stores();  // the codes and the scale are in the XCC's L2 before the count
   sync(atid & 63);
@@ -606,15 +754,18 @@ SVG_DEV void act_copy_stage(const PassStep& S, const Geo& g, PassLds& L, int M, 
 
 // Sum the stream waves' partials of tile t (fixed order) and store y; split
 // steps exchange the halves through the workspace (one act wave does it all).
-SVG_DEV void finish_tile(const PassStep& S, const Geo& g, PassLds& L, int slot, int t, int M, u32* ws, int lane) {
+// `dot`: the partials are the dot-product form's (one per row and wave),
+// else the matrix-core form's (16 tokens x 16 rows per wave).
+SVG_DEV void finish_tile(const PassStep& S, const Geo& g, PassLds& L, int slot, int t, int M, bool dot, u32* ws,
+                         int lane) {
   const float* part = L.part[slot];
-  if (M == 1 && !S.split) {
+  if (dot) {
     if (lane < 16) {
       float v = 0.f;
       for (int w = 0; w < kStreamWaves; ++w) v += part[w * 16 + lane];
       const int n = t * 16 + lane;
       if (n < S.N)
-        __hip_atomic_store(S.y + n, L.xs[0] * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gstore_dev(S.y + n, L.xs[0] * v);
     }
     return;
   }
@@ -631,7 +782,7 @@ SVG_DEV void finish_tile(const PassStep& S, const Geo& g, PassLds& L, int slot, 
     const float* other = reinterpret_cast<const float*>(ws + S.part_off) + ((size_t)t * 2 + (g.h ^ 1)) * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __hip_atomic_store(mine + lane + 64 * i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gstore_dev(mine + lane + 64 * i, v[i]);
     wait_stores();
     u32 old = 0;
     if (lane == 0) old = add_dev(ws + S.tcnt_off + t, 1u);
@@ -639,7 +790,7 @@ SVG_DEV void finish_tile(const PassStep& S, const Geo& g, PassLds& L, int slot, 
     if (old == 0) return;  // the other half finishes the tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float o = __hip_atomic_load(other + lane + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float o = gload_dev(other + lane + 64 * i);
       v[i] = g.h == 0 ? v[i] + o : o + v[i];
     }
     if (lane == 0) st_dev(ws + S.tcnt_off + t, 0u);
@@ -648,7 +799,7 @@ SVG_DEV void finish_tile(const PassStep& S, const Geo& g, PassLds& L, int slot, 
   for (int i = 0; i < 4; ++i) {
     const int o = lane + 64 * i, m = o >> 4, n = t * 16 + (o & 15);
     if (m < M && n < S.N)
-      __hip_atomic_store(S.y + (size_t)m * S.N + n, L.xs[m] * v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gstore_dev(S.y + (size_t)m * S.N + n, L.xs[m] * v[i]);
   }
 }
 
@@ -662,77 +813,118 @@ SVG_DEV void quant_m1_any(const PassStep& S, PassLds& L, int atid, int awave, Ac
 // ------------------------------------------------------------- the ring
 template <int G, bool Z4, bool MFMA>
 struct StreamCtx {
-  PassLds* L;
   const PassStep* plan;
-  u32* ws;
   u32* trace;
-  int M, wave, lane, b;
-  u32 lane16;
+  int nsteps, M, wave, lane, b;
+  u32 lane16, lanep;
   Issuer<G, Z4> iss;
   Consumer<G, Z4> con;
   u32x4 W[kRing];
-  u32 Sc[kRing], Zr[kRing];
+  typename Issuer<G, Z4>::SType Sc[kRing];
+  typename Issuer<G, Z4>::ZType Zr[kRing];
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  u32 seq = 0;  // tiles this workgroup has finished
+  u32 seq = 0;  // tile slots this workgroup has finished
+
+  SVG_DEV void uniform() {
+    nsteps = uni(nsteps);
+    M = uni(M);
+    wave = uni(wave);
+    seq = uni(seq);
+    iss.uniform();
+    con.uniform();
+  }
+  // Wait until the codes of the step the consumer has just entered are in
+  // LDS (M = 1: first until every stream wave is done with the previous row).
+  SVG_DEV void wait_codes() {
+    if constexpr (!MFMA) wg_barrier();
+    wg_barrier();
+    if (wave == 0 && lane == 0) trace_at(trace, con.p.j, 3);
+  }
 };
 
 // Slot S of the ring, unrolled by recursion so that every register of the
-// ring is named statically: consume the chunk in slot S, then load the
-// chunk kRing positions ahead into it.
+// ring is named statically: compute the chunk in slot S, load the chunk
+// kRing positions ahead into it, then move the consumer on (at the end of a
+// tile slot: hand the partials over; on entering a step: wait for its codes,
+// with this slot's load already on its way).
+//
+// The end of the sequence is tested in slot 0 only, and every slot issues its
+// loads on every path (past the end they load zeros without touching
+// memory), so on every path from a slot's loads back to that slot the same
+// number of loads follow them: the compiler's wait before each chunk leaves
+// the other kRing - 1 chunks in flight.  (An exit from the middle of the turn
+// would join the loop's back edge with fewer loads behind the slot and force
+// a wait for all of them.)  Past the end a slot computes on zeros from LDS
+// offsets at most kRing chunks past the last row's end (inside the
+// workgroup's LDS) and hands nothing over.
 template <int G, bool Z4, bool MFMA, int S>
 struct RingSlot {
+  static SVG_DEV void load(StreamCtx<G, Z4, MFMA>& x) {
+    x.iss.issue(x.W[S], x.Sc[S], x.Zr[S]);
+    x.iss.advance(x.plan, x.nsteps, x.wave, x.lane16, x.lanep);
+  }
   static SVG_DEV void prime(StreamCtx<G, Z4, MFMA>& x) {
-    x.iss.issue(x.W[S], x.Sc[S], x.Zr[S], x.lane16, x.con.r);
-    x.iss.next();
+    load(x);
     if constexpr (S + 1 < kRing) RingSlot<G, Z4, MFMA, S + 1>::prime(x);
   }
-  // false once the sequence has ended
+  // One turn; false once the sequence has ended.
   static SVG_DEV bool run(StreamCtx<G, Z4, MFMA>& x) {
     Consumer<G, Z4>& it = x.con;
-    if (it.w.at_end()) return false;
-    if (it.w.ti == 0 && it.w.c == 0) {  // first chunk of a step: wait for its activation codes
-      if constexpr (!MFMA) wg_barrier();  // M = 1: the previous step's LDS row is free
-      wg_barrier();                         // the new codes are in LDS
-      if (x.wave == 0 && x.lane == 0) trace_at(x.trace, it.w.j, 3);
+    if constexpr (S == 0) {
+      x.uniform();
+      if (it.p.j >= x.nsteps) return false;
     }
-    const int8_t* act = reinterpret_cast<const int8_t*>(x.L->act);
+    const bool live = S == 0 || it.p.j < x.nsteps;
+    const int8_t* act = reinterpret_cast<const int8_t*>(g_lds.act);
     if constexpr (MFMA) compute_mfma<G, Z4>(it, x.W[S], x.Sc[S], x.Zr[S], act, x.M, x.b, x.acc);
     else compute_dot<G, Z4>(it, x.W[S], x.Sc[S], x.Zr[S], act, x.b, x.acc[0]);
-    if (it.w.c == it.w.cpw - 1) {  // this wave's last chunk of the tile: hand the partials over
-      const u32 slot = x.seq % kSlots, use = x.seq / kSlots;
-      lds_wait_ge(&x.L->consumed[slot], use, x.ws);
-      float* part = x.L->part[slot];
-      if constexpr (MFMA) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[x.wave * 256 + (4 * x.b + i) * 16 + it.r] = x.acc[i];
-      } else {
-        float v = x.acc[0];
-        v += lane_xorf<16>(v);
-        v += __int_as_float(lane_xor32(__float_as_int(v)));
-        if (x.b == 0) part[x.wave * 16 + it.r] = v;
-      }
-      lds_fence();
-      if (x.lane == 0) lds_add(&x.L->ready[slot], 1u);
-      x.acc[0] = x.acc[1] = x.acc[2] = x.acc[3] = 0.f;
-      ++x.seq;
-      if (x.wave == 0 && x.lane == 0 && it.w.ti == it.w.g.ntw - 1) trace_at(x.trace, it.w.j, 7);
+    load(x);
+    if (live) {
+      ++it.jj;
+      if (--it.p.left == 0 && hand_over(x)) x.wait_codes();
     }
-    it.take(it.w.advance());
-    x.iss.issue(x.W[S], x.Sc[S], x.Zr[S], x.lane16, it.r);
-    x.iss.next();
     if constexpr (S + 1 < kRing) return RingSlot<G, Z4, MFMA, S + 1>::run(x);
     else return true;
+  }
+  // The wave's last chunk of a tile slot is in: its partials go to the
+  // slot's LDS entry (once the act wave has summed the entry's previous use).
+  // Returns true when the walk entered a new step.
+  static SVG_DEV bool hand_over(StreamCtx<G, Z4, MFMA>& x) {
+    Consumer<G, Z4>& it = x.con;
+    const u32 slot = x.seq % kSlots, use = x.seq / kSlots;
+    lds_wait_ge(&g_lds.consumed[slot], use);  // a give-up shows on the act side
+    float* part = g_lds.part[slot];
+    if constexpr (MFMA) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[x.wave * 256 + (4 * x.b + i) * 16 + it.r] = x.acc[i];
+    } else {
+      float v = x.acc[0];
+      v += lane_xorf<16>(v);
+      v += __int_as_float(lane_xor32(__float_as_int(v)));
+      if (x.b == 0) part[x.wave * 16 + it.r] = v;
+    }
+    lds_fence();
+    if (x.lane == 0) lds_add(&g_lds.ready[slot], 1u);
+    x.acc[0] = x.acc[1] = x.acc[2] = x.acc[3] = 0.f;
+    ++x.seq;
+    if (x.wave == 0 && x.lane == 0 && it.p.ti == it.p.nts - 1) trace_at(x.trace, it.p.j, 7);
+    const int n = it.p.next_tile(x.plan, x.nsteps, x.wave);
+    it.p.uniform();
+    it.take(x.plan, n == 1);
+    return n == 1;
   }
 };
 
 // ------------------------------------------------------------------ kernel
 template <int G, bool Z4, bool MFMA>
 __global__ __launch_bounds__(kThreads, 1) void k_pass(const PassHdr* __restrict__ hdr_p, u32* ws) {
-  __shared__ PassLds L;
+  PassLds& L = g_lds;
   const PassHdr H = *hdr_p;
   const PassStep* plan = reinterpret_cast<const PassStep*>(hdr_p + 1);
   const int nsteps = H.nsteps, M = H.M;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform over the wave: say so, so that everything the
+  // walks derive from it (and the step table loads) stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const u32 xcc = hw_xcc();
   if (threadIdx.x < kSlots) {
     L.ready[threadIdx.x] = 0u;
@@ -747,22 +939,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_pass(const PassHdr* __restrict_
   if (wave < kStreamWaves) {
     // ------------------------------------------------------ stream waves
     StreamCtx<G, Z4, MFMA> x;
-    x.L = &L;
     x.plan = plan;
-    x.ws = ws;
     x.trace = H.trace;
+    x.nsteps = nsteps;
     x.M = M;
     x.wave = wave;
     x.lane = lane;
     x.b = lane >> 4;
     x.lane16 = (u32)lane * 16u;
-    x.iss.w = Walk{plan, nsteps, wave};
-    x.iss.take(x.iss.w.enter(0));
-    x.con.w = x.iss.w;
+    x.lanep = (u32)(lane & 15) * (u32)Issuer<G, Z4>::GPB;
+    x.iss.take(plan, x.iss.p.enter(plan, nsteps, wave, 0), x.lane16, x.lanep);
     x.con.r = lane & 15;
-    x.con.take(x.con.w.enter(0));
+    x.con.p = x.iss.p;
+    x.con.take(plan, true);                 // step 0 (the pass has at least one step)
     RingSlot<G, Z4, MFMA, 0>::prime(x);   // the issue side runs kRing chunks ahead
     if (M > 1) wg_barrier();               // start: the XCC ranks are known
+    x.wait_codes();
     while (RingSlot<G, Z4, MFMA, 0>::run(x)) {
     }
   } else {
@@ -784,12 +976,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_pass(const PassHdr* __restrict_
     ActSync sync{&L.act_sync, ws, 0u};
     for (int j = 0; j < nsteps; ++j) {
       const PassStep& S = plan[j];
-      const Geo g = step_geo(S, 0);
+      const Geo g = step_geo(S);
       if constexpr (!MFMA) {  // M = 1: each workgroup quantizes the row it needs
-        if (g.ntw == 0) {
-          if (atid == 0) last = arrive(ws, j, nsteps);
-          continue;
-        }
         if (atid == 0) trace_at(H.trace, j, 0);
         wg_barrier();  // the stream waves are done with the previous step's LDS row
         if (waits(S, j, M)) {  // every earlier step counted complete
@@ -803,7 +991,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pass(const PassHdr* __restrict_
           trace_at(H.trace, j, 2);
           trace_at(H.trace, j, 4);
         }
-      } else {  // M >= 2: rows quantized once per XCC, by workgroups with or without tiles
+      } else if constexpr (MFMA) {  // M >= 2: rows quantized once per XCC, by workgroups with or without tiles
         if (atid == 0) trace_at(H.trace, j, 0);
         if (waits(S, j, M)) {
           if (atid == 0) poll_ge(step_count(ws, j - 1), (u32)(gridDim.x < 8 ? gridDim.x : 8), ws);
@@ -814,23 +1002,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_pass(const PassHdr* __restrict_
           if (H.block == 64) act_quant_row_stage<64>(S, L, m, M, ws, H, xcc, j, atid, awave, sync);
           else act_quant_row_stage<32>(S, L, m, M, ws, H, xcc, j, atid, awave, sync);
         }
-        if (g.ntw == 0) {
-          if (atid == 0) last = arrive(ws, j, nsteps);
-          continue;
-        }
         if (atid == 0) trace_at(H.trace, j, 2);
         if ((atid & 63) == 0) poll_ge(ws + kLine * (H.qbase + 2 * j) + 16 * xcc, (u32)M, ws);
         act_copy_stage(S, g, L, M, ws, H, xcc, atid);
         wg_barrier();  // the codes are in LDS
         if (atid == 0) trace_at(H.trace, j, 4);
       }
-      // tiles: act wave s sums the partials of slot s once all stream waves are in
-      for (int ti = 0; ti < g.ntw; ++ti, ++seq) {
+      // tile slots: act wave s sums the partials of LDS slot s once all stream
+      // waves are in (and stores y for a real tile)
+      for (int ti = 0; ti < g.nts; ++ti, ++seq) {
         const u32 slot = seq % kSlots, use = seq / kSlots;
         if (awave != (int)slot) continue;
-        lds_wait_ge(&L.ready[slot], kStreamWaves * (use + 1), ws);
+        if (lds_wait_ge(&L.ready[slot], kStreamWaves * (use + 1))) st_dev(ws, 1u);
         asm volatile("" ::: "memory");
-        finish_tile(S, g, L, slot, g.t0 + ti * g.ts, M, ws, lane);
+        const int t = g.t0 + ti * g.ts;
+        if (t < g.tlim) finish_tile(S, g, L, slot, t, M, !MFMA, ws, lane);
         lds_fence();
         if (lane == 0) __hip_atomic_store(&L.consumed[slot], use + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
@@ -840,7 +1026,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pass(const PassHdr* __restrict_
       if (lane == 0) lds_add(&L.act_done, 1u);
       ++steps_done;
       if (atid == 0) {
-        lds_wait_ge(&L.act_done, 4u * steps_done, ws);
+        if (lds_wait_ge(&L.act_done, 4u * steps_done)) st_dev(ws, 1u);
         last = arrive(ws, j, nsteps);
         trace_at(H.trace, j, 6);
       }
