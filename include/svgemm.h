@@ -397,6 +397,48 @@ svg_status svg_pass_plan(const svg_pass_step* steps, int nsteps, int M, int fmt,
                          void* plan_host, uint64_t plan_host_bytes, svg_pass_info* info);
 svg_status svg_pass_run(const void* plan, const svg_pass_info* info, void* workspace, void* stream);
 
+/*
+ * Layout conversions between the canonical row-major arrays and the storage
+ * the kernels read.  [KT "How Uzu optimizes bytes and tokens per pass": 4-bit
+ * asymmetric codes with a scale and zero per group, 8-bit symmetric codes
+ * with one scale per row, 8-bit activations -- the pages fix no layout; the
+ * canonical one is the plainest row-major reading.]
+ *
+ * Canonical arrays (device memory, owned by the caller):
+ *   W4 codes    [N][K/2] bytes: code (n, k) in byte n*K/2 + k/2, low nibble
+ *               for even k, high nibble for odd k
+ *   W4 scales   [N][K/group] fp16 (bit patterns)
+ *   fp16 zeros  [N][K/group] fp16 (SVG_W4_ASYM_Z16; integer values 0..15)
+ *   4-bit zeros [N][ceil(K/group/2)] bytes: zero (n, j) in byte
+ *               n*ceil(K/group/2) + j/2, low nibble for even j (SVG_W4_ASYM_Z4)
+ *   W8 codes    [N][K] int8;  W8 scales [N] fp16 (zero: NULL)
+ *   act codes   [M][K] int8
+ *
+ *  svg_import_weights  canonical (codes, scale, zero) -> storage (wq, w_scale,
+ *                      w_zero, sized by svg_weight_sizes; padding written 0).
+ *                      The result is what rht_rotate_weights writes for the
+ *                      same codes, scales and zeros.
+ *  svg_export_weights  storage -> canonical (the inverse on the real rows
+ *                      and groups).
+ *  svg_import_act_codes  [M][K] rows -> xq in the 32-k slab layout of a
+ *                      buffer of M rows (as act_rht_quant_i8 writes it).
+ *  svg_export_act_codes  slab xq of M rows -> [M][K] rows.
+ * Asynchronous on `stream`; pure data movement (no rotation, no rounding).
+ * Errors (checked before any launch, outputs untouched): SVG_EINVAL for N, M
+ * < 0, K <= 0 or a null required pointer (W4: zero and w_zero required);
+ * SVG_EUNSUPPORTED for an unknown fmt, K % 32 != 0, a W4 group not in {32,
+ * 64, 128} or not dividing K, K > 2^24, storage of 4 GiB or more, M*K >= 2^34;
+ * SVG_EALIGN for wq or xq below 16 bytes, w_scale / fp16 w_zero below 4,
+ * canonical fp16 arrays below 2, activation rows below 4.  Inputs and outputs
+ * must not overlap.
+ */
+svg_status svg_import_weights(int fmt, int group, int N, int K, const void* codes, const uint16_t* scale,
+                              const void* zero, void* wq, uint16_t* w_scale, void* w_zero, void* stream);
+svg_status svg_export_weights(int fmt, int group, int N, int K, const void* wq, const uint16_t* w_scale,
+                              const void* w_zero, void* codes, uint16_t* scale, void* zero, void* stream);
+svg_status svg_import_act_codes(const int8_t* rows, int M, int K, int8_t* xq, void* stream);
+svg_status svg_export_act_codes(const int8_t* xq, int M, int K, int8_t* rows, void* stream);
+
 /* Text of the last error on the calling thread ("" after a successful call);
  * valid until the next call on this thread. */
 const char* svg_last_error(void);

@@ -54,6 +54,10 @@ def _load():
         fn.restype = ctypes.c_int
     lib.svg_pass_plan.argtypes = [vp, i, i, i, i, i, vp, ctypes.c_uint64, vp]
     lib.svg_pass_run.argtypes = [vp, vp, vp, vp]
+    lib.svg_import_weights.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.svg_export_weights.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.svg_import_act_codes.argtypes = [vp, i, i, vp, vp]
+    lib.svg_export_act_codes.argtypes = [vp, i, i, vp, vp]
     lib.svg_pass_plan.restype = ctypes.c_int
     lib.svg_pass_run.restype = ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
@@ -321,6 +325,70 @@ def tree_deltanet_commit(state, k, v, alpha, beta, path, n_emit, stream=None):
         raise ValueError("path needs T - 1 entries and n_emit one")
     _check(lib.tree_deltanet_commit(_p(state), _p(k), _p(v), _p(alpha), _p(beta), _p(path), _p(n_emit),
                                     T, H, dk, dv, _stream(stream, state)))
+
+
+# ------------------------------------------------------- layout conversions
+def _check_canonical(N, K, f, group, codes, scale, zero):
+    if f == W8:
+        _dev(codes, "codes", torch.int8)
+        if tuple(codes.shape) != (N, K) or tuple(scale.shape) != (N,):
+            raise ValueError("W8: codes must be [N, K] int8 and scale [N] fp16")
+    else:
+        _dev(codes, "codes", torch.uint8)
+        ng = K // group
+        if tuple(codes.shape) != (N, K // 2) or tuple(scale.shape) != (N, ng):
+            raise ValueError("W4: codes must be [N, K/2] uint8 and scale [N, K/group] fp16")
+        if zero is None:
+            raise ValueError("W4 formats need zero")
+        if f == W4_Z4:
+            _dev(zero, "zero", torch.uint8)
+            if tuple(zero.shape) != (N, (ng + 1) // 2):
+                raise ValueError("4-bit zeros must be [N, ceil(K/group/2)] uint8")
+        else:
+            _dev(zero, "zero", torch.float16)
+            if tuple(zero.shape) != (N, ng):
+                raise ValueError("fp16 zeros must be [N, K/group]")
+    _dev(scale, "scale", torch.float16)
+
+
+def import_weights(codes, scale, zero, fmt, group, K, wq, w_scale, w_zero=None, stream=None):
+    """Canonical row-major weights (codes, scale, zero) -> the tiled storage
+    (wq, w_scale, w_zero) sized by weight_sizes()."""
+    f = _fmt(fmt)
+    N = codes.shape[0]
+    _check_canonical(N, K, f, group, codes, scale, zero)
+    _check_storage(N, K, f, group, wq, w_scale, w_zero)
+    _check(lib.svg_import_weights(f, group, N, K, _p(codes), _p(scale), _p(zero), _p(wq), _p(w_scale),
+                                  _p(w_zero), _stream(stream, wq)))
+
+
+def export_weights(wq, w_scale, w_zero, fmt, group, N, K, codes, scale, zero=None, stream=None):
+    """The tiled storage -> canonical row-major (codes, scale, zero)."""
+    f = _fmt(fmt)
+    _check_canonical(N, K, f, group, codes, scale, zero)
+    _check_storage(N, K, f, group, wq, w_scale, w_zero)
+    _check(lib.svg_export_weights(f, group, N, K, _p(wq), _p(w_scale), _p(w_zero), _p(codes), _p(scale),
+                                  _p(zero), _stream(stream, wq)))
+
+
+def import_act_codes(rows, xq, stream=None):
+    """Activation codes [M, K] int8 rows -> xq in the slab layout."""
+    _dev(rows, "rows", torch.int8)
+    _dev(xq, "xq", torch.int8)
+    M, K = rows.shape
+    if xq.numel() != M * K:
+        raise ValueError("xq must hold M * K codes")
+    _check(lib.svg_import_act_codes(_p(rows), M, K, _p(xq), _stream(stream, rows)))
+
+
+def export_act_codes(xq, rows, stream=None):
+    """xq in the slab layout -> activation codes [M, K] int8 rows."""
+    _dev(rows, "rows", torch.int8)
+    _dev(xq, "xq", torch.int8)
+    M, K = rows.shape
+    if xq.numel() != M * K:
+        raise ValueError("xq must hold M * K codes")
+    _check(lib.svg_export_act_codes(_p(xq), M, K, _p(rows), _stream(stream, rows)))
 
 
 def empty_weights(N, K, fmt, group, device="cuda"):

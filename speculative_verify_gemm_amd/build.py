@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsvgemm.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["rht_quant.hip", "linear_w4.hip", "linear_w8.hip", "tree_accept.hip", "tree_deltanet.hip",
-           "pass.hip", "svgemm.hip"]
+           "pass.hip", "layout.hip", "svgemm.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -54,6 +54,15 @@ const char* svg_pass_check(const svg_pass_step* steps, int nsteps, int M, int fm
 void svg_pass_write(const svg_pass_step* steps, int nsteps, int M, int fmt, int group, int block, void* plan_host);
 hipError_t svg_launch_pass(const void* plan, int M, int fmt, int group, void* ws, hipStream_t stream);
 
+// Layout conversions (layout.hip): canonical row-major arrays <-> storage.
+hipError_t svg_launch_import_weights(int fmt_w8, int z4, int group, int N, int K, const void* codes,
+                                     const uint16_t* scale, const void* zero, void* wq, uint16_t* w_scale,
+                                     void* w_zero, hipStream_t stream);
+hipError_t svg_launch_export_weights(int fmt_w8, int z4, int group, int N, int K, const void* wq,
+                                     const uint16_t* w_scale, const void* w_zero, void* codes, uint16_t* scale,
+                                     void* zero, hipStream_t stream);
+hipError_t svg_launch_act_codes(int to_slab, const int8_t* src, int M, int K, int8_t* dst, hipStream_t stream);
+
 // Bytes of the weight storage (include/svgemm.h describes the layout).
 // W4 codes: tiled, rows padded to 16 and K to 128.  Scales and zeros:
 // blocked per (16-row tile, 512-k block, row), rows padded to 16 and K to

@@ -361,3 +361,82 @@ svg_status tree_deltanet_commit(float* state, const float* k, const float* v, co
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------ layout conversions
+namespace {
+// The checks both weight conversions share; `codes`, `scale` and `zero` are
+// the canonical arrays, the others the storage.
+svg_status weight_layout_check(const char* fn, int fmt, int group, int N, int K, const void* codes,
+                               const uint16_t* scale, const void* zero, const void* wq, const uint16_t* w_scale,
+                               const void* w_zero) {
+  if (N < 0) return fail(SVG_EINVAL, fn, "N < 0");
+  if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
+  if (fmt != SVG_W4_ASYM_Z4 && fmt != SVG_W4_ASYM_Z16 && fmt != SVG_W8_SYM)
+    return fail(SVG_EUNSUPPORTED, fn, "unknown fmt");
+  if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  const bool w4 = fmt != SVG_W8_SYM;
+  if (w4 && !group_ok(group)) return fail(SVG_EUNSUPPORTED, fn, "group must be 32, 64 or 128");
+  if (w4 && K % group) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of group");
+  if (K > kMaxK) return fail(SVG_EUNSUPPORTED, fn, "K > 2^24");
+  if (w4 ? !fits_w4(N, K, group, fmt == SVG_W4_ASYM_Z4) : !fits_w8(N, K))
+    return fail(SVG_EUNSUPPORTED, fn, "weight storage of 4 GiB or more: split the matrix along N");
+  if ((uint64_t)N * (uint64_t)K >= (1ull << 40)) return fail(SVG_EUNSUPPORTED, fn, "N * K too large");
+  if (!codes || !scale || !wq || !w_scale || (w4 && (!zero || !w_zero)))
+    return fail(SVG_EINVAL, fn, "null required pointer");
+  if (!aligned(wq, 16)) return fail(SVG_EALIGN, fn, "wq needs 16-byte alignment");
+  if (!aligned(w_scale, 4) || (fmt == SVG_W4_ASYM_Z16 && !aligned(w_zero, 4)))
+    return fail(SVG_EALIGN, fn, "w_scale / fp16 w_zero need 4-byte alignment");
+  if (!aligned(scale, 2) || (fmt == SVG_W4_ASYM_Z16 && !aligned(zero, 2)))
+    return fail(SVG_EALIGN, fn, "the fp16 scale / zero rows need 2-byte alignment");
+  return SVG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+svg_status svg_import_weights(int fmt, int group, int N, int K, const void* codes, const uint16_t* scale,
+                              const void* zero, void* wq, uint16_t* w_scale, void* w_zero, void* stream) {
+  static const char* fn = "svg_import_weights";
+  const svg_status st = weight_layout_check(fn, fmt, group, N, K, codes, scale, zero, wq, w_scale, w_zero);
+  if (st != SVG_OK) return st;
+  if (N == 0) return ok();
+  return hip_status(fn, svg_launch_import_weights(fmt == SVG_W8_SYM, fmt == SVG_W4_ASYM_Z4, group, N, K, codes,
+                                                  scale, zero, wq, w_scale, w_zero,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status svg_export_weights(int fmt, int group, int N, int K, const void* wq, const uint16_t* w_scale,
+                              const void* w_zero, void* codes, uint16_t* scale, void* zero, void* stream) {
+  static const char* fn = "svg_export_weights";
+  const svg_status st = weight_layout_check(fn, fmt, group, N, K, codes, scale, zero, wq, w_scale, w_zero);
+  if (st != SVG_OK) return st;
+  if (N == 0) return ok();
+  return hip_status(fn, svg_launch_export_weights(fmt == SVG_W8_SYM, fmt == SVG_W4_ASYM_Z4, group, N, K, wq,
+                                                  w_scale, w_zero, codes, scale, zero,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+static svg_status act_layout(const char* fn, int to_slab, const int8_t* src, int M, int K, int8_t* dst,
+                             void* stream) {
+  if (M < 0) return fail(SVG_EINVAL, fn, "M < 0");
+  if (K <= 0) return fail(SVG_EINVAL, fn, "K <= 0");
+  if (K % 32) return fail(SVG_EUNSUPPORTED, fn, "K must be a multiple of 32");
+  if ((uint64_t)M * (uint64_t)K >= (1ull << 34)) return fail(SVG_EUNSUPPORTED, fn, "M * K too large");
+  if (!src || !dst) return fail(SVG_EINVAL, fn, "null required pointer");
+  const int8_t* slab = to_slab ? dst : src;
+  const int8_t* rows = to_slab ? src : dst;
+  if (!aligned(slab, 16)) return fail(SVG_EALIGN, fn, "the slab codes need 16-byte alignment");
+  if (!aligned(rows, 4)) return fail(SVG_EALIGN, fn, "the code rows need 4-byte alignment");
+  if (M == 0) return ok();
+  return hip_status(fn, svg_launch_act_codes(to_slab, src, M, K, dst, reinterpret_cast<hipStream_t>(stream)));
+}
+
+svg_status svg_import_act_codes(const int8_t* rows, int M, int K, int8_t* xq, void* stream) {
+  return act_layout("svg_import_act_codes", 1, rows, M, K, xq, stream);
+}
+
+svg_status svg_export_act_codes(const int8_t* xq, int M, int K, int8_t* rows, void* stream) {
+  return act_layout("svg_export_act_codes", 0, xq, M, K, rows, stream);
+}
+
+}  // extern "C"

@@ -61,12 +61,12 @@ def gpu_linear(xq, xs, w, debug=True):
 
 def oracle_storage(ow, fmt, K):
     """The oracle's encoded weights in the library's tiled storage (host arrays)."""
-    from oracle import svg_oracle as O
+    import storage_layout as SL
     if fmt == "w8":
-        return O.pack_w8_codes(ow["q"]), ow["s"], None
+        return SL.pack_w8_codes(ow["q"]), ow["s"], None
     g = ow["group"]
-    z = O.pack_z4(ow["z"], K, g) if fmt == "w4_z4" else O.zeros_as_f16(ow["z"], K, g)
-    return O.pack_w4_codes(ow["q"]), O.tile_group_params(ow["s"], K, g), z
+    z = SL.pack_z4(ow["z"], K, g) if fmt == "w4_z4" else SL.zeros_as_f16(ow["z"], K, g)
+    return SL.pack_w4_codes(ow["q"]), SL.tile_group_params(ow["s"], K, g), z
 
 
 def oracle_weights_to_dev(ow, fmt):

@@ -30,6 +30,7 @@ def svg():
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
         ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
+         "svg_export_act_codes", "svg_export_weights", "svg_import_act_codes", "svg_import_weights",
          "svg_last_error", "svg_pass_plan", "svg_pass_run", "svg_weight_sizes", "tree_accept_greedy", "tree_accept_greedy_static",
          "tree_deltanet_commit",
          "tree_deltanet_verify", "w4a8_linear", "w8a8_linear"])
@@ -157,18 +158,18 @@ def test_fused_empty_calls_are_ok(svg):
 
 def test_weight_sizes_match_the_oracle_layout(svg):
     import numpy as np
-    from oracle import svg_oracle as O
+    import storage_layout as SL
     for N, K, fmt, g in [(37, 384, "w4_z4", 32), (12288, 4096, "w4_z16", 64), (20, 384, "w4_z16", 128), (20, 320, "w4_z16", 64),
                          (5, 96, "w4_z4", 32), (45, 1120, "w8", 0), (16, 64, "w8", 0)]:
         wb, sb, zb = svg.weight_sizes(N, K, fmt, g)
         if fmt == "w8":
-            assert wb == O.pack_w8_codes(np.zeros((N, K), np.int8)).nbytes and sb == 2 * N and zb == 0
+            assert wb == SL.pack_w8_codes(np.zeros((N, K), np.int8)).nbytes and sb == 2 * N and zb == 0
         else:
             q = np.zeros((N, K), np.uint8)
             z = np.zeros((N, K // g), np.uint8)
-            assert wb == O.pack_w4_codes(q).nbytes
-            assert sb == O.tile_group_params(z.astype(np.float16), K, g).nbytes
-            zref = O.pack_z4(z, K, g) if fmt == "w4_z4" else O.zeros_as_f16(z, K, g)
+            assert wb == SL.pack_w4_codes(q).nbytes
+            assert sb == SL.tile_group_params(z.astype(np.float16), K, g).nbytes
+            zref = SL.pack_z4(z, K, g) if fmt == "w4_z4" else SL.zeros_as_f16(z, K, g)
             assert zb == zref.nbytes
     with pytest.raises(svg.SvgError):
         svg.weight_sizes(16, 48, "w4_z16", 64)
@@ -328,3 +329,54 @@ def test_pass_run_validation(svg):
     assert svg.lib.svg_pass_run(A, ctypes.byref(info), ctypes.c_void_p(0x10080), NULL) == 3   # not 256-aligned
     bad = svg.PassInfoC(2, 17, 1, 64, 32, info.plan_bytes, info.workspace_bytes)
     assert svg.lib.svg_pass_run(A, ctypes.byref(bad), A, NULL) == 2
+
+
+# ------------------------------------------------------ layout conversions
+def _imp(svg, export=False, **kw):
+    args = dict(fmt=1, g=64, N=16, K=128, codes=A, scale=A, zero=A, wq=A, ws=A, wz=A)
+    args.update(kw)
+    fn = svg.lib.svg_export_weights if export else svg.lib.svg_import_weights
+    if export:
+        return fn(args["fmt"], args["g"], args["N"], args["K"], args["wq"], args["ws"], args["wz"],
+                  args["codes"], args["scale"], args["zero"], NULL)
+    return fn(args["fmt"], args["g"], args["N"], args["K"], args["codes"], args["scale"], args["zero"],
+              args["wq"], args["ws"], args["wz"], NULL)
+
+
+@pytest.mark.parametrize("export", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(codes=NULL), 1), (dict(scale=NULL), 1), (dict(zero=NULL), 1), (dict(wq=NULL), 1), (dict(ws=NULL), 1),
+    (dict(wz=NULL), 1), (dict(N=-1), 1), (dict(K=0), 1),
+    (dict(fmt=7), 2), (dict(K=48), 2), (dict(g=16), 2), (dict(K=96, g=64), 2), (dict(K=1 << 25), 2),
+    (dict(wq=MIS), 3), (dict(ws=ctypes.c_void_p(0x10002)), 3), (dict(wz=ctypes.c_void_p(0x10002)), 3),
+    (dict(scale=MIS), 3), (dict(zero=MIS), 3),
+])
+def test_weight_layout_calls_validate_before_any_launch(svg, export, kw, code):
+    """Every invalid call is refused on the host with its status code (the
+    pointers are never dereferenced: no device work is enqueued)."""
+    assert _imp(svg, export, **kw) == code, (kw, svg.last_error())
+
+
+def test_weight_layout_calls_accept_w8_without_zeros(svg):
+    # W8 needs no zero arrays; N = 0 is a no-op that touches nothing
+    assert _imp(svg, fmt=2, g=0, N=0, zero=NULL, wz=NULL) == 0
+    assert _imp(svg, True, fmt=2, g=0, N=0, zero=NULL, wz=NULL) == 0
+    # a 4-bit zero array is bytes: any alignment
+    assert _imp(svg, fmt=0, N=0, zero=MIS, wz=MIS) == 0
+    assert _imp(svg, fmt=1, N=0) == 0
+
+
+@pytest.mark.parametrize("name", ["svg_import_act_codes", "svg_export_act_codes"])
+def test_act_layout_calls_validate_before_any_launch(svg, name):
+    fn = getattr(svg.lib, name)
+    assert fn(NULL, 1, 64, A, NULL) == 1
+    assert fn(A, 1, 64, NULL, NULL) == 1
+    assert fn(A, -1, 64, A, NULL) == 1
+    assert fn(A, 1, 0, A, NULL) == 1
+    assert fn(A, 1, 48, A, NULL) == 2
+    slab_mis = (MIS, A) if name == "svg_export_act_codes" else (A, MIS)
+    assert fn(slab_mis[0], 2, 64, slab_mis[1], NULL) == 3
+    rows_mis = ctypes.c_void_p(0x10002)
+    args = (A, 2, 64, rows_mis) if name == "svg_export_act_codes" else (rows_mis, 2, 64, A)
+    assert fn(*args, NULL) == 3
+    assert fn(A, 0, 64, A, NULL) == 0  # M = 0: nothing to do

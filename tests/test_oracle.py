@@ -22,6 +22,7 @@ import pytest
 import synth
 from oracle import brute
 from oracle import svg_oracle as O
+import storage_layout as SL
 
 
 def _read_golden(path):
@@ -324,8 +325,8 @@ def _w4_byte_and_nibble(n, k, K):
 def test_w4_tiled_layout_element_by_element(N, K):
     rng = np.random.default_rng(N * K)
     q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
-    packed = O.pack_w4_codes(q)
-    Np, Kp = O.w4_tiled_shape(N, K)
+    packed = SL.pack_w4_codes(q)
+    Np, Kp = SL.w4_tiled_shape(N, K)
     assert packed.size == Np * Kp // 2
     seen = np.zeros(packed.size * 2, bool)
     for n in range(N):
@@ -341,7 +342,7 @@ def test_w4_tiled_layout_element_by_element(N, K):
 def test_w4_tiled_layout_worked_example():
     # row 0, k = 0..127 with code k % 16: piece 0 holds k 0..15 then 64..79.
     q = (np.arange(128) % 16).astype(np.uint8)[None, :]
-    p = O.pack_w4_codes(q)
+    p = SL.pack_w4_codes(q)
     assert p[:8].tolist() == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
     assert p[8:16].tolist() == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
     assert not p[16:256].any()          # pieces of rows 1..15 (padding)
@@ -354,8 +355,8 @@ def test_group_params_blocked_element_by_element(N, K, group):
     G = K // group
     a = rng.integers(1, 1000, size=(N, G)).astype(np.float16)
     z = rng.integers(0, 16, size=(N, G)).astype(np.uint8)
-    t = O.tile_group_params(a, K, group)
-    z4 = O.pack_z4(z, K, group)
+    t = SL.tile_group_params(a, K, group)
+    z4 = SL.pack_z4(z, K, group)
     gpb = 512 // group
     KB = -(-K // 512)
     Np = -(-N // 16) * 16
@@ -372,7 +373,7 @@ def test_group_params_blocked_element_by_element(N, K, group):
 def test_z4_pack_by_hand():
     z = np.zeros((1, 8), dtype=np.uint8)
     z[0, :3] = [3, 12, 5]
-    p = O.pack_z4(z, 512, 64)
+    p = SL.pack_z4(z, 512, 64)
     assert p[:2].tolist() == [0xC3, 0x05] and not p[2:].any()
 
 
@@ -380,7 +381,7 @@ def test_z4_pack_by_hand():
 def test_w8_tiled_layout_element_by_element(N, K):
     rng = np.random.default_rng(N + K)
     q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
-    p = O.pack_w8_codes(q)
+    p = SL.pack_w8_codes(q)
     KT = -(-K // 64)
     for n in range(N):
         for k in range(K):
@@ -393,7 +394,7 @@ def test_w8_tiled_layout_element_by_element(N, K):
 def test_act_slab_layout_element_by_element(M, K):
     rng = np.random.default_rng(M * 1000 + K)
     q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
-    p = O.pack_act_codes(q)
+    p = SL.pack_act_codes(q)
     assert p.size == M * K
     for m in range(M):
         for k in range(K):
@@ -403,13 +404,13 @@ def test_act_slab_layout_element_by_element(M, K):
 def test_act_slab_layout_worked_example():
     # two tokens, K = 64: slab 0 holds token 0's k 0..31 then token 1's k 0..31
     q = np.arange(128, dtype=np.int64).reshape(2, 64).astype(np.int8)
-    p = O.pack_act_codes(q)
+    p = SL.pack_act_codes(q)
     assert p[:32].tolist() == list(range(0, 32))
     assert p[32:64].tolist() == list(range(64, 96))
     assert p[64:96].tolist() == list(range(32, 64))
     assert p[96:].tolist() == [v - 256 if v > 127 else v for v in range(96, 128)]
     one = q[:1]
-    assert np.array_equal(O.pack_act_codes(one), one.reshape(-1))  # one token: the row itself
+    assert np.array_equal(SL.pack_act_codes(one), one.reshape(-1))  # one token: the row itself
 
 
 # ------------------------------------------------------- contraction pins
@@ -498,11 +499,11 @@ def test_linear_bytes_counts_real_arrays(fmt, group):
     x, W, signs = synth.random_case(M, N, K, seed=1)
     if fmt == "w8":
         w = O.prepare_w8(W, signs)
-        wbytes = O.pack_w8_codes(w["q"]).nbytes + w["s"].nbytes
+        wbytes = SL.pack_w8_codes(w["q"]).nbytes + w["s"].nbytes
     else:
         w = O.prepare_w4(W, signs, group)
-        z = O.pack_z4(w["z"], K, group) if fmt == "w4_z4" else O.zeros_as_f16(w["z"], K, group)
-        wbytes = (O.pack_w4_codes(w["q"]).nbytes + O.tile_group_params(w["s"], K, group).nbytes
+        z = SL.pack_z4(w["z"], K, group) if fmt == "w4_z4" else SL.zeros_as_f16(w["z"], K, group)
+        wbytes = (SL.pack_w4_codes(w["q"]).nbytes + SL.tile_group_params(w["s"], K, group).nbytes
                   + z.nbytes)
     qx, sx = O.quant_acts(x, signs)
     y = np.zeros((M, N), np.float32)

@@ -17,6 +17,7 @@ torch = pytest.importorskip("torch")
 
 import synth
 from oracle import svg_oracle as O
+import storage_layout as SL
 from oracle import tree_oracle as TO
 
 pytestmark = pytest.mark.gpu
@@ -58,7 +59,7 @@ def test_act_codes_bit_exact(M, K, src):
             x[1] = 0.0  # an all-zero token
     qx, sx = O.quant_acts(x, signs)
     xq, xs = C.gpu_quant_acts(x, signs)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
 
 
@@ -118,7 +119,7 @@ def test_linear_matches_oracle(fmt, group, M, N, K):
         ow = O.prepare_w4(W, signs, group)
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
     w = C.oracle_weights_to_dev(ow, fmt)
-    y, dbg = C.gpu_linear(C.to_dev(O.pack_act_codes(qx).reshape(qx.shape)), C.to_dev(sx), w)
+    y, dbg = C.gpu_linear(C.to_dev(SL.pack_act_codes(qx).reshape(qx.shape)), C.to_dev(sx), w)
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
 
@@ -167,10 +168,10 @@ def test_full_size_single_matrix(src):
     w = C.gpu_prepare(W, signs, fmt, g)
     xq, xs = C.gpu_quant_acts(x, signs)
     y, dbg = C.gpu_linear(xq, xs, w)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
-    assert np.array_equal(C.host(w["wq"]), O.pack_w4_codes(ow["q"]))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
+    assert np.array_equal(C.host(w["wq"]), SL.pack_w4_codes(ow["q"]))
     assert np.array_equal(C.host(w["ws"]).view(np.uint16),
-                          O.tile_group_params(ow["s"], x.shape[1], g).view(np.uint16))
+                          SL.tile_group_params(ow["s"], x.shape[1], g).view(np.uint16))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
 
@@ -196,7 +197,7 @@ def test_w8_partials_reach_the_int32_bound():
     assert (S_ref == 127 * 127 * K).all()
     w = C.gpu_prepare(W, signs, "w8", 0)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert (C.host(dbg).astype(np.int64) == 127 * 127 * K).all()
     check_y(C.host(y), y_ref)
 
@@ -213,7 +214,7 @@ def test_w4_long_k(M):
     y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
     w = C.gpu_prepare(W, signs, "w4_z16", g)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
@@ -236,7 +237,7 @@ def test_act_codes_extreme_rows():
     x = _scaled_rows(x, [1e-42, 1e-39, 1e-30, 1.0, 1e30, 1e36])
     qx, sx = O.quant_acts(x, signs)
     xq, xs = C.gpu_quant_acts(x, signs)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
 
 
@@ -280,7 +281,7 @@ def test_linear_extreme_rows(fmt, group, M):
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, O.prepare_w4(W, signs, group))
     w = C.gpu_prepare(W, signs, fmt, group)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
 
@@ -446,12 +447,12 @@ def test_act_codes_at_rounding_ties(nudge):
     x, signs = C.tie_rows(M, K, seed=5 + int(nudge), nudge=nudge)
     qx, sx = O.quant_acts(x, signs)
     xq, xs = C.gpu_quant_acts(x, signs)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     _x, W, _s = synth.random_case(1, N, K, seed=77)
     w = C.oracle_weights_to_dev(O.prepare_w4(W, signs, 64), "w4_z16")
     fq, fs, _y, _d = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(fq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(fq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(fs).view(np.uint32), sx.view(np.uint32))
 
 
@@ -481,7 +482,7 @@ def test_fused_matches_oracle(fmt, group, M, N, K):
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
     w = C.oracle_weights_to_dev(ow, fmt)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
     check_y(C.host(y), y_ref)
@@ -598,12 +599,36 @@ def test_stack_launch_sampled_rows(workload, M, launch):
         y_ref, S_ref, qx, sx = O.linear_w8(x, signs, O.prepare_w8(Wr, signs))
     else:
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, O.prepare_w4(Wr, signs, group))
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     assert np.array_equal(C.host(dbg)[:, rows].astype(np.int64), S_ref)
     yh = C.host(y)
     check_y(yh[:, rows], y_ref)
     assert np.array_equal(C.host(y2).view(np.uint32), yh.view(np.uint32))
+
+
+@pytest.mark.parametrize("workload,M", [("stack_w4g64", 16), ("stack_w8", 32)])
+def test_stack_o_launch_every_output(workload, M):
+    """The o projection of the stack (4096 x 4096) at the verify batch of its
+    format, issued as bench.py issues it, against the oracle on EVERY output:
+    the per-group partial sums of all M x 4096 outputs bit-exact and all of y
+    within tolerance (one full-size launch of each matrix-core policy)."""
+    spec = synth.WORKLOADS[workload]
+    fmt, group = spec["fmt"], spec["group"]
+    w, Ws, signs, space = C.stack_launch(0, "o", fmt, group)
+    N, K = w["N"], w["K"]
+    C.say(f"stack o launch, every output: {workload} M={M} N={N} K={K}")
+    x = synth.stack_acts(workload, 0, space, M)
+    xq, xs, y, dbg = C.gpu_fused(x, signs, w)
+    W = C.stacked_rows(Ws, list(range(N)))
+    if fmt == "w8":
+        y_ref, S_ref, qx, sx = O.linear_w8(x, signs, O.prepare_w8(W, signs))
+    else:
+        y_ref, S_ref, qx, sx = O.linear_w4(x, signs, O.prepare_w4(W, signs, group))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
+    assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
+    assert np.array_equal(C.host(dbg).astype(np.int64), S_ref)
+    check_y(C.host(y), y_ref)
 
 
 # ------------------------------------------- the wave-wide transform block
@@ -618,7 +643,7 @@ def test_act_codes_block64(M, K):
     x, _W, signs = synth.random_case(M, 1, K, seed=M * 31 + K, x_kind="student_t3")
     qx, sx = O.quant_acts(x, signs, 64)
     xq, xs = C.gpu_quant_acts(x, signs, block=64)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
 
 
@@ -659,7 +684,7 @@ def test_linear_block64_end_to_end(fmt, group, M, N, K):
     ow = O.prepare_w8(W, signs, 64) if fmt == "w8" else O.prepare_w4(W, signs, group, 64)
     y_ref, S, qx, sx = (O.linear_w8 if fmt == "w8" else O.linear_w4)(x, signs, ow)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
-    assert np.array_equal(C.host(xq).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(xq).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(xs).view(np.uint32), sx.view(np.uint32))
     assert np.array_equal(C.host(dbg).astype(np.int64), S)
     check_y(C.host(y), y_ref)

@@ -22,6 +22,7 @@ torch = pytest.importorskip("torch")
 
 import synth
 from oracle import svg_oracle as O
+import storage_layout as SL
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +61,7 @@ def _step(M, N, K, fmt, group, seed, block=32, after=1, debug=True, x=None):
 
 def _check_step(st, ref, M):
     y_ref, S_ref, qx, sx = O.linear_w4(ref["x"], ref["signs"], ref["ow"])
-    assert np.array_equal(C.host(st["xq"]).reshape(-1), O.pack_act_codes(qx))
+    assert np.array_equal(C.host(st["xq"]).reshape(-1), SL.pack_act_codes(qx))
     assert np.array_equal(C.host(st["x_scale"]).view(np.uint32), sx.view(np.uint32))
     if "partials_debug" in st:
         assert np.array_equal(C.host(st["partials_debug"]).astype(np.int64), S_ref)
@@ -200,7 +201,7 @@ def test_pass_on_a_stack_layer(M):
         W = C.stacked_rows(Ws, rows)
         ow = O.prepare_w4(W, signs, group)
         y_ref, S_ref, qx, sx = O.linear_w4(x, signs, ow)
-        assert np.array_equal(C.host(st["xq"]).reshape(-1), O.pack_act_codes(qx))
+        assert np.array_equal(C.host(st["xq"]).reshape(-1), SL.pack_act_codes(qx))
         assert np.array_equal(C.host(st["x_scale"]).view(np.uint32), sx.view(np.uint32))
         assert np.array_equal(C.host(st["partials_debug"])[:, rows].astype(np.int64), S_ref)
         check_y(C.host(st["y"])[:, rows], y_ref)
