@@ -211,6 +211,40 @@ class Stack:
         return g
 
 
+def measure_workload(workload, Ms, args, dev, torch, kernel_m=None):
+    """Passes of another workload of the stack at several M (its own weights,
+    built on the device and freed afterwards): per M the pass time, achieved
+    GB/s and fraction of the HBM peak, and the committed counter summary of
+    its HBM traffic (or why there is none).  With kernel_m, the linear
+    launches at that M are timed as for the headline workload too."""
+    stack = Stack(workload, args.layers, dev, block=args.block)
+    res = {"description": WORKLOADS[workload]["desc"], "passes": []}
+    for m in Ms:
+        io = stack.make_inputs(m)
+        g = stack.capture(io)
+        ms, med, mn = time_graph(torch, g, args.steps, args.warmup, dev)
+        nb = stack.pass_bytes(m)
+        gbps = nb / (ms * 1e-3) / 1e9
+        traffic, src = profiled_traffic(workload, m)
+        row = {"M": m, "ms_per_pass": round(ms, 5), "ms_per_pass_median": round(med, 5),
+               "GB_per_s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+               "bytes_per_pass": nb, "traffic_bytes_per_launch": round(traffic) if traffic else None,
+               "traffic_source": src}
+        if m == kernel_m:
+            kms, kb, _n, kmed = time_linear_launches(stack, io, g, ms, max(1, min(args.steps, 7)))
+            kg = kb / (kms * 1e-3) / 1e9
+            row["roofline"] = {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, m, stack.fused),
+                               "achieved": round(kg, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                               "frac": round(kg / PEAK_HBM_GBPS, 4), "mean_launch_us": round(kms * 1e3, 3),
+                               "mean_launch_us_by_kind": kmed}
+        print(f"[bench] {workload} M={m}: {ms:.4f} ms/pass, {gbps:.1f} GB/s", file=sys.stderr, flush=True)
+        res["passes"].append(row)
+        del g, io
+    del stack
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_graph(torch, g, steps, warmup, dev):
     """Replay the captured pass: `warmup` untimed, then `steps` timed between
     HIP events on the replay stream.  Returns (mean, median, min) ms per pass;
@@ -634,6 +668,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the M=1 comparison pass")
     ap.add_argument("--sweep", default=None, help="comma-separated M values: report a pass per M")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the W8 (M=32) stack and the g128 M sweep reported beside the headline")
     ap.add_argument("--block", type=int, default=32, choices=(32, 64),
                     help="transform block: the pages' 32, or the wave-wide 64")
     ap.add_argument("--tree-vocab", type=int, default=131072,
@@ -760,6 +796,31 @@ def main():
         print(f"[bench] linears alone per layer: M=1 {t1:.2f} us, M={M} {t16:.2f} us (x{t16 / t1:.3f})",
               file=sys.stderr, flush=True)
         del g1
+    if not args.no_configs and args.workload == "stack_w4g64":
+        # the other configurations of the stack, timed in the same run: W8 at
+        # its verify batch, and the g128 stack over the verify batch sizes
+        out["config_w8_m32"] = measure_workload("stack_w8", [32], args, dev, torch, kernel_m=32)
+        c5 = measure_workload("stack_w4g128", [1, 2, 4, 8, 16, 32], args, dev, torch)
+        t1 = c5["passes"][0]["ms_per_pass"]
+        for row in c5["passes"]:
+            row["over_m1"] = round(row["ms_per_pass"] / t1, 4)
+        out["config_w4g128_sweep"] = c5
+    # the targets this line is measured against, pass or fail
+    targets = {}
+    if "decode_m1" in out:
+        f1 = out["decode_m1"]["frac_of_hbm_peak"]
+        targets["decode_m1_frac_of_hbm_peak"] = {"measured": f1, "threshold": 0.80, "rule": ">=",
+                                                 "pass": f1 >= 0.80}
+        r = out.get(f"verify_m{M}_over_decode_m1")
+        targets[f"verify_m{M}_over_decode_m1"] = {"measured": r, "threshold": 1.30, "rule": "<=",
+                                                  "pass": r is not None and r <= 1.30}
+    if "config_w4g128_sweep" in out:
+        for row in out["config_w4g128_sweep"]["passes"]:
+            if row["M"] in (2, 4, 8):
+                targets[f"w4g128_m{row['M']}_over_m1"] = {"measured": row["over_m1"], "threshold": 1.10,
+                                                          "rule": "<=", "pass": row["over_m1"] <= 1.10}
+    if targets:
+        out["targets"] = targets
     if args.sweep:
         rows = []
         for m in [int(v) for v in args.sweep.split(",")]:
