@@ -80,12 +80,16 @@ def weight_bytes(N, K, fmt, group):
 class Stack:
     """The synthetic stack resident on the device, and its captured passes."""
 
-    def __init__(self, workload, layers, dev, fused=True, block=32, engine="launches"):
+    def __init__(self, workload, layers, dev, fused=True, block=32, engine="launches", shared=False):
         import torch
         import speculative_verify_gemm_amd as svg
         import synth
         self.torch, self.svg, self.synth = torch, svg, synth
         self.fused = fused
+        # the fused calls' workspace: verify-batch rows quantized inside the
+        # linear's own launch (None: in a launch of their own)
+        self.shared = shared and fused
+        self.ws = svg.linear_workspace(dev) if self.shared else None
         self.block = block
         self.engine = engine
         self.wl = workload
@@ -138,10 +142,10 @@ class Stack:
             X, sg = io["xin"][L][space], self.signs[L][space]
             xq, xs, y = io["xq"][space], io["xs"][space], io["ys"][L][name]
             if self.fmt == "w8":
-                self.svg.act_quant_w8a8_linear(X, sg, xq, xs, wq, ws, N, y, block=self.block)
+                self.svg.act_quant_w8a8_linear(X, sg, xq, xs, wq, ws, N, y, block=self.block, workspace=self.ws)
             else:
                 self.svg.act_quant_w4a8_linear(X, sg, xq, xs, wq, ws, wz, self.fmt, self.group, N, y,
-                                               block=self.block)
+                                               block=self.block, workspace=self.ws)
             return
         if self.fmt == "w8":
             self.svg.w8a8_linear(io["xq"][space], io["xs"][space], wq, ws, N, io["ys"][L][name])
@@ -217,7 +221,7 @@ def measure_workload(workload, Ms, args, dev, torch, kernel_m=None):
     GB/s and fraction of the HBM peak, and the committed counter summary of
     its HBM traffic (or why there is none).  With kernel_m, the linear
     launches at that M are timed as for the headline workload too."""
-    stack = Stack(workload, args.layers, dev, block=args.block)
+    stack = Stack(workload, args.layers, dev, block=args.block, shared=args.shared_quant)
     res = {"description": WORKLOADS[workload]["desc"], "passes": []}
     for m in Ms:
         io = stack.make_inputs(m)
@@ -233,7 +237,7 @@ def measure_workload(workload, Ms, args, dev, torch, kernel_m=None):
         if m == kernel_m:
             kms, kb, _n, kmed = time_linear_launches(stack, io, g, ms, max(1, min(args.steps, 7)))
             kg = kb / (kms * 1e-3) / 1e9
-            row["roofline"] = {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, m, stack.fused),
+            row["roofline"] = {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, m, stack.fused, stack.shared),
                                "achieved": round(kg, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                "frac": round(kg / PEAK_HBM_GBPS, 4), "mean_launch_us": round(kms * 1e3, 3),
                                "mean_launch_us_by_kind": kmed}
@@ -278,7 +282,7 @@ def time_linear_launches(stack, io, g, ms_graph, steps, unfused=False):
     With `unfused` the linear alone is timed at every M.
     Returns (mean ms, mean algorithmic bytes, launches, {kind: mean us})."""
     torch = stack.torch
-    fused = stack.fused and one_launch(io["M"], stack.group) and not unfused
+    fused = stack.fused and one_launch(io["M"], stack.group, stack.shared) and not unfused
     t0 = time.perf_counter()
     stack.run_pass(io)                       # host cost of enqueuing one eager pass
     enqueue_ms = (time.perf_counter() - t0) * 1e3
@@ -310,15 +314,16 @@ def time_linear_launches(stack, io, g, ms_graph, steps, unfused=False):
             {n: round(v * 1e3, 3) for n, v in mean_kind.items()})
 
 
-def one_launch(M, group):
-    """Whether act_quant_*_linear quantizes inside the linear's launch."""
-    return M == 1 or (M <= 2 and group == 32)
+def one_launch(M, group, shared=False):
+    """Whether act_quant_*_linear quantizes inside the linear's launch (with a
+    workspace: at every M but for 32-wide W4 groups past M = 2)."""
+    return M == 1 or (M <= 2 and group == 32) or (shared and group != 32)
 
 
-def kernel_name(fmt, group, M, fused):
+def kernel_name(fmt, group, M, fused, shared=False):
     """The linear kernel template instance a launch of this format and M runs
-    (k_linear[_fused]<policy, waves, chunks per wave, batch>; the shape varies
-    with K)."""
+    (k_linear[_fused|_shared]<policy, waves, chunks per wave, batch>; the
+    shape varies with K)."""
     if fmt == "w8":
         pol = "DotW8<1>" if M <= 1 else f"MfmaW8<{1 if M <= 16 else 2}>"
     else:
@@ -327,6 +332,8 @@ def kernel_name(fmt, group, M, fused):
             pol = f"DotW4<{1 if M <= 1 else 2 if M <= 2 else 8}, {group}, {z4}, false>"
         else:
             pol = f"MfmaW4<{1 if M <= 16 else 2}, {group}, {z4}, false>"
+    if fused and shared and M > 1 and group != 32:
+        return f"k_linear_shared<{pol}, ...>"
     return f"k_linear{'_fused' if fused and one_launch(M, group) else ''}<{pol}, ...>"
 
 
@@ -663,6 +670,10 @@ def main():
     ap.add_argument("--workload", default="stack_w4g64", choices=sorted(WORKLOADS) + sorted(SINGLE))
     ap.add_argument("--m", type=int, default=None, help="tokens per pass (default: the workload's)")
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--shared-quant", action="store_true",
+                    help="verify batches: quantize the rows inside the linear's launch (the _ws calls) instead "
+                         "of in a launch of their own (measured slower: the in-launch hand-off costs more than "
+                         "the launch)")
     ap.add_argument("--unfused", action="store_true",
                     help="quantize activations in a launch of their own before each linear")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -701,7 +712,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize(dev)
         del src, dst
-    stack = Stack(args.workload, args.layers, dev, fused=not args.unfused, block=args.block)
+    stack = Stack(args.workload, args.layers, dev, fused=not args.unfused, block=args.block,
+                  shared=args.shared_quant)
     print(f"[bench] weights resident after {stack.setup_s:.1f} s", file=sys.stderr, flush=True)
 
     def measure(m):
@@ -721,7 +733,7 @@ def main():
           file=sys.stderr, flush=True)
     traffic, traffic_src = profiled_traffic(args.workload, M)
     read_us = read_kernel_times(args.workload)
-    one = stack.fused and one_launch(M, stack.group)
+    one = stack.fused and one_launch(M, stack.group, stack.shared)
     ops_per_pass = sum(2 * M * N * K for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
     kops = ops_per_pass / (args.layers * len(LAYER_LAUNCHES))  # mean int ops per linear launch
     wbytes = sum(weight_bytes(N, K, stack.fmt, stack.group) for _n, _m, N, K, _s in LAYER_LAUNCHES) * args.layers
@@ -752,7 +764,7 @@ def main():
         "tokens_per_s_ceiling": {"tau_1": round(1e3 / ms, 1), f"tau_{M}": round(M * 1e3 / ms, 1),
                                  # the pages' measured tokens per verify pass on their machine: context only
                                  "tau_8.39_pages_context": round(8.39 * 1e3 / ms, 1)},
-        "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M, stack.fused),
+        "roofline": {"bound": "hbm", "kernel": kernel_name(stack.fmt, stack.group, M, stack.fused, stack.shared),
                      "achieved": round(k_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic else None,

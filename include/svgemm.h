@@ -224,6 +224,38 @@ svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* sig
                                  int32_t* partials_debug, void* stream);
 
 /*
+ * act_quant_w4a8_linear_ws / act_quant_w8a8_linear_ws -- the fused calls
+ * with a workspace: for a verify batch (M >= 2, the MFMA forms; or a row
+ * longer than the single-row fused kernel takes) the rows are rotated and
+ * quantized inside the linear's own launch, once: workgroup m (m < M) writes
+ * row m into xq / x_scale before it requests any weights, and every
+ * workgroup requests its first weight batch, then waits for all M rows before
+ * it reads activation codes.  No launch of its own for the quantization,
+ * for callers that want one launch per linear; on MI355X the hand-off inside
+ * the launch (about 5 us from launch to the last row visible at M = 16,
+ * K = 4096) measured slower than the two-launch path.  [KT "Producing several tokens from one model pass": one
+ * verification pass runs the linears on 16-32 candidate rows; "Why
+ * batch-one decoding is memory-bound": the pass should cost its bytes.]
+ * Arguments, outputs and errors as for act_quant_w4a8_linear /
+ * act_quant_w8a8_linear (32-wide W4 groups at M > 2 keep the separate
+ * quantization launch), plus:
+ *  workspace  SVG_LINEAR_WORKSPACE_BYTES of device memory, 256-byte aligned,
+ *             zero-filled before its first use; each call leaves it zero-
+ *             filled again except word 3, a sticky flag set (to 1) if a
+ *             bounded wait of the launch ever gave up (then y is
+ *             undefined).  Calls that may overlap need different workspaces.
+ *  Errors: SVG_EINVAL for a null workspace, SVG_EALIGN for a misaligned one.
+ */
+#define SVG_LINEAR_WORKSPACE_BYTES 256
+svg_status act_quant_w4a8_linear_ws(const float* X, int M, int K, const int8_t* signs, int block,
+                                    int8_t* xq, float* x_scale, const uint8_t* wq, const uint16_t* w_scale,
+                                    const void* w_zero, int fmt, int group, int N, float* y,
+                                    int32_t* partials_debug, void* workspace, void* stream);
+svg_status act_quant_w8a8_linear_ws(const float* X, int M, int K, const int8_t* signs, int block,
+                                    int8_t* xq, float* x_scale, const int8_t* wq, const uint16_t* w_scale,
+                                    int N, float* y, int32_t* partials_debug, void* workspace, void* stream);
+
+/*
  * tree_accept_greedy -- greedy acceptance of a verified draft tree.
  * [KT "Producing several tokens from one model pass": the main model checks the
  *  drafted positions together, keeps the valid prefix and continues from the

@@ -43,6 +43,8 @@ def _load():
     lib.w8a8_linear.argtypes = [vp, vp, i, i, vp, vp, i, vp, vp, vp]
     lib.act_quant_w4a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp]
     lib.act_quant_w8a8_linear.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, i, vp, vp, vp]
+    lib.act_quant_w4a8_linear_ws.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp]
+    lib.act_quant_w8a8_linear_ws.argtypes = [vp, i, i, vp, i, vp, vp, vp, vp, i, vp, vp, vp, vp]
     lib.tree_accept_greedy.argtypes = [vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.tree_accept_greedy_static.argtypes = [vp, i, i, vp, vp, vp, vp, vp, vp, vp]
     lib.tree_deltanet_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp]
@@ -206,9 +208,11 @@ def _check_fused(X, signs, xq, x_scale):
 
 
 def act_quant_w4a8_linear(X, signs, xq, x_scale, wq, w_scale, w_zero, fmt, group, N, y,
-                          partials_debug=None, block=BLOCK, stream=None):
+                          partials_debug=None, block=BLOCK, stream=None, workspace=None):
     """act_rht_quant_i8 then w4a8_linear (one launch for M = 1): fp32 X[M, K]
-    in, xq / x_scale (written) and y[M, N] out."""
+    in, xq / x_scale (written) and y[M, N] out.  With a workspace (from
+    linear_workspace()) the rows of a verify batch are quantized inside the
+    linear's own launch (act_quant_w4a8_linear_ws)."""
     _check_fused(X, signs, xq, x_scale)
     f = _fmt(fmt)
     _dev(xq, "xq", torch.int8)
@@ -222,14 +226,21 @@ def act_quant_w4a8_linear(X, signs, xq, x_scale, wq, w_scale, w_zero, fmt, group
         _dev(partials_debug, "partials_debug", torch.int32)
         if tuple(partials_debug.shape) != (M, N, K // group):
             raise ValueError("partials_debug must be [M, N, K/g]")
+    if workspace is not None:
+        _check_linear_workspace(workspace)
+        _check(lib.act_quant_w4a8_linear_ws(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale), _p(wq),
+                                            _p(w_scale), _p(w_zero), f, group, N, _p(y), _p(partials_debug),
+                                            _p(workspace), _stream(stream, X)))
+        return
     _check(lib.act_quant_w4a8_linear(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale), _p(wq),
                                      _p(w_scale), _p(w_zero), f, group, N, _p(y), _p(partials_debug),
                                      _stream(stream, X)))
 
 
 def act_quant_w8a8_linear(X, signs, xq, x_scale, wq, w_scale, N, y, partials_debug=None,
-                          block=BLOCK, stream=None):
-    """act_rht_quant_i8 then w8a8_linear (one launch for M = 1)."""
+                          block=BLOCK, stream=None, workspace=None):
+    """act_rht_quant_i8 then w8a8_linear (one launch for M = 1; with a
+    workspace, one launch at every M: act_quant_w8a8_linear_ws)."""
     _check_fused(X, signs, xq, x_scale)
     _dev(xq, "xq", torch.int8)
     _dev(x_scale, "x_scale", torch.float32)
@@ -242,11 +253,37 @@ def act_quant_w8a8_linear(X, signs, xq, x_scale, wq, w_scale, N, y, partials_deb
         _dev(partials_debug, "partials_debug", torch.int32)
         if tuple(partials_debug.shape) != (M, N):
             raise ValueError("partials_debug must be [M, N]")
+    if workspace is not None:
+        _check_linear_workspace(workspace)
+        _check(lib.act_quant_w8a8_linear_ws(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale), _p(wq),
+                                            _p(w_scale), N, _p(y), _p(partials_debug), _p(workspace),
+                                            _stream(stream, X)))
+        return
     _check(lib.act_quant_w8a8_linear(_p(X), M, K, _p(signs), block, _p(xq), _p(x_scale), _p(wq),
                                      _p(w_scale), N, _p(y), _p(partials_debug), _stream(stream, X)))
 
 
 # ------------------------------------------------------------- allocation
+LINEAR_WORKSPACE_BYTES = 256
+
+
+def linear_workspace(device="cuda"):
+    """A zero-filled workspace for the fused calls' in-launch quantization
+    (each call leaves it zero-filled, word 3 excepted: a sticky give-up flag;
+    calls that may overlap need workspaces of their own)."""
+    return torch.zeros(LINEAR_WORKSPACE_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def _check_linear_workspace(ws):
+    _dev(ws, "workspace", torch.int32)
+    if ws.numel() * 4 < LINEAR_WORKSPACE_BYTES:
+        raise ValueError(f"workspace needs {LINEAR_WORKSPACE_BYTES} bytes")
+
+
+def linear_workspace_gave_up(ws) -> bool:
+    """Whether a bounded wait of a call on this workspace ever gave up."""
+    return int(ws[3].item()) != 0
+
 
 TREE_MAX_NODES, TREE_WORKSPACE_BYTES = 32, 512
 

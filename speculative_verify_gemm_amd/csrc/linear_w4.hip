@@ -184,15 +184,16 @@ struct MfmaW4 : W4Common {
       for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
   }
 
-  template <int NC, bool LDS = false>
+  // AUX: cache policy of the loads (kSC1: rows published in this launch)
+  template <int NC, bool LDS = false, int AUX = 0>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
     static_assert(!LDS, "the MFMA policy reads its activation rows from global memory");
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int h = 0; h < MH; ++h) {
-        X.a1[c][h] = bload16(xr, x_off(h * 16 + r, j0 + c, 0));
-        X.a2[c][h] = bload16(xr, x_off(h * 16 + r, j0 + c, 1));
+        X.a1[c][h] = bload16a<AUX>(xr, x_off(h * 16 + r, j0 + c, 0));
+        X.a2[c][h] = bload16a<AUX>(xr, x_off(h * 16 + r, j0 + c, 1));
       }
   }
 
@@ -305,7 +306,7 @@ struct DotW4 : W4Common {
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
   }
 
-  template <int NC, bool LDS = false>
+  template <int NC, bool LDS = false, int AUX = 0>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -318,8 +319,8 @@ struct DotW4 : W4Common {
           X.a1[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(row) : zero;
           X.a2[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(row + 64) : zero;
         } else {
-          X.a1[c][m] = bload16(xr, x_off(m, j0 + c, 0));
-          X.a2[c][m] = bload16(xr, x_off(m, j0 + c, 1));
+          X.a1[c][m] = bload16a<AUX>(xr, x_off(m, j0 + c, 0));
+          X.a2[c][m] = bload16a<AUX>(xr, x_off(m, j0 + c, 1));
         }
       }
   }
@@ -447,9 +448,9 @@ hipError_t dispatch_g(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
                            float* y, int32_t* dbg, const float* X, const int8_t* signs, int block,
-                           hipStream_t stream) {
+                           uint32_t* ws, hipStream_t stream) {
   const LinArgs a{xq, x_scale, M, K, wq, w_scale, w_zero, N, y, dbg, M, 0};
-  const ActIn fa{X, signs, block};
+  const ActIn fa{X, signs, block, ws};
   const ActIn* f = X ? &fa : nullptr;
 #define SVG_G_CASE(G)                                                                                  \
   if (group == G) {                                                                                    \

@@ -101,7 +101,7 @@ struct DotW8 : W8Common {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0;
   }
-  template <int NC, bool LDS = false>
+  template <int NC, bool LDS = false, int AUX = 0>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -112,7 +112,7 @@ struct DotW8 : W8Common {
           const u32x4 zero = {0u, 0u, 0u, 0u};
           X.a[c][m] = j < KT ? *reinterpret_cast<const u32x4*>(xlds + m * xlds_row + j * 64 + 16 * b) : zero;
         } else {
-          X.a[c][m] = bload16(xr, x_off(m, j0 + c));
+          X.a[c][m] = bload16a<AUX>(xr, x_off(m, j0 + c));
         }
       }
   }
@@ -173,13 +173,13 @@ struct MfmaW8 : W8Common {
 #pragma unroll
     for (int h = 0; h < MH; ++h) acc[h] = v4i{0, 0, 0, 0};
   }
-  template <int NC, bool LDS = false>
+  template <int NC, bool LDS = false, int AUX = 0>
   SVG_DEV void load_acts(Acts<NC>& X, int j0) const {
     static_assert(!LDS, "the MFMA policy reads its activation rows from global memory");
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int h = 0; h < MH; ++h) X.a[c][h] = bload16(xr, x_off(h * 16 + r, j0 + c));
+      for (int h = 0; h < MH; ++h) X.a[c][h] = bload16a<AUX>(xr, x_off(h * 16 + r, j0 + c));
   }
   template <int U>
   SVG_DEV void load(Batch<U>& B, int t, int j0, bool valid) const {
@@ -217,9 +217,9 @@ struct MfmaW8 : W8Common {
 
 hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
-                           const int8_t* signs, int block, hipStream_t stream) {
+                           const int8_t* signs, int block, uint32_t* ws, hipStream_t stream) {
   const LinArgs a{xq, x_scale, M, K, wq, w_scale, nullptr, N, y, dbg, M, 0};
-  const ActIn fa{X, signs, block};
+  const ActIn fa{X, signs, block, ws};
   const ActIn* f = X ? &fa : nullptr;
   if (M <= 1) return launch_linear_auto<DotW8<1>>(a, f, stream);
   if (M <= 16) return launch_linear_auto<MfmaW8<1>>(a, f, stream);

@@ -73,7 +73,6 @@ constexpr int kSlots = 4;                 // tile partial slots (one per act wav
 constexpr int kStageRow = kPassMaxK;      // bytes per row of an XCC staging copy
 constexpr int kXcc = 8;                   // counter groups (and XCC staging copies)
 constexpr u32 kPollLimit = 1u << 20;      // device polls before a wait gives up (about a second)
-constexpr int kSC1 = 16;                  // cache policy: device scope (sc1)
 constexpr u32 kMagic = 0x53564750u;       // plan image header
 
 // The device image of one step (svg_pass_plan writes it on the host).

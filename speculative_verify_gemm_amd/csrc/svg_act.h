@@ -99,18 +99,22 @@ SVG_DEV u32 pack4(const int q[4]) {
 
 // Where act_quant_row puts its results: packed code words and the row scale.
 // StoreGlobal: row m of a global code buffer of ldm rows in 32-k slabs
-// (include/svgemm.h).  StoreLds: a row of LDS words in k order.
-struct StoreGlobal {
+// (include/svgemm.h); AUX is the stores' cache policy (kSC1: written through
+// for readers on other XCCs in the same launch).  StoreLds: a row of LDS
+// words in k order.
+template <int AUX>
+struct StoreGlobalT {
   rsrc_t out, sc;
   u32 m, ldm;
-  SVG_DEV StoreGlobal(int8_t* xq, int m_, int ldm_, float* scale, int K)
+  SVG_DEV StoreGlobalT(int8_t* xq, int m_, int ldm_, float* scale, int K)
       : out(make_rsrc(xq, (u32)ldm_ * (u32)K)), sc(make_rsrc(scale, 4u)), m((u32)m_), ldm((u32)ldm_) {}
   // word c holds k = 4c .. 4c + 3: slab c / 8, bytes 4 (c % 8) of the row's 32
   SVG_DEV void word(u32 c, u32 v) const {
-    __builtin_amdgcn_raw_buffer_store_b32(v, out, ((c >> 3) * ldm + m) * 32u + 4u * (c & 7u), 0u, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(v, out, ((c >> 3) * ldm + m) * 32u + 4u * (c & 7u), 0u, AUX);
   }
-  SVG_DEV void scale(float v) const { __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), sc, 0u, 0u, 0); }
+  SVG_DEV void scale(float v) const { __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), sc, 0u, 0u, AUX); }
 };
+using StoreGlobal = StoreGlobalT<0>;
 
 struct StoreLds {
   u32* row;     // LDS, K/4 words

@@ -120,11 +120,14 @@ SVG_DEV float half_bits_to_float(uint16_t h) { return __half2float(__ushort_as_h
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr u32 kOOB = 0x80000000u;      // beyond every buffer this library builds
 constexpr int kNT = 2;                 // cache policy: non-temporal (streamed once)
+constexpr int kSC1 = 16;               // cache policy: device scope (sc1: past the caches of one XCC)
 SVG_DEV rsrc_t make_rsrc(const void* base, u32 nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)nbytes, 0x00020000);
 }
 SVG_DEV u32x4 bload16(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
 SVG_DEV u32x4 bload16_nt(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT); }
+template <int AUX>
+SVG_DEV u32x4 bload16a(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX); }
 SVG_DEV u32 bload4(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
 SVG_DEV uint16_t bload2(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
 SVG_DEV uint8_t bload1(rsrc_t r, u32 off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }

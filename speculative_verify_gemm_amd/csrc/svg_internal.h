@@ -20,10 +20,10 @@ hipError_t svg_launch_rot_quant_w8(const float* W, int N, int K, const int8_t* s
 hipError_t svg_launch_w4a8(const int8_t* xq, const float* x_scale, int M, int K, const uint8_t* wq,
                            const uint16_t* w_scale, const void* w_zero, bool z4, int group, int N,
                            float* y, int32_t* dbg, const float* X, const int8_t* signs, int block,
-                           hipStream_t stream);
+                           uint32_t* ws, hipStream_t stream);
 hipError_t svg_launch_w8a8(const int8_t* xq, const float* x_scale, int M, int K, const int8_t* wq,
                            const uint16_t* w_scale, int N, float* y, int32_t* dbg, const float* X,
-                           const int8_t* signs, int block, hipStream_t stream);
+                           const int8_t* signs, int block, uint32_t* ws, hipStream_t stream);
 
 // Greedy acceptance of a draft tree (tree_accept.hip); `workspace` is the
 // caller's zero-filled SVG_TREE_WORKSPACE_BYTES, left zero-filled.

@@ -92,7 +92,7 @@ struct TileSteps {
 // rows are being quantized.  (With global activations the second batch waits:
 // loads complete in order, so activations requested after it would hold the
 // first computation back.)
-template <class P, int CPW, int U, bool LDS, class Pre, class Gate>
+template <class P, int CPW, int U, bool LDS, int AUX, class Pre, class Gate>
 SVG_DEV void stream_tiles_resident(P& p, int ntiles, int first, int stride, Pre&& pre, Gate&& gate) {
   static_assert(CPW % U == 0, "batches must tile a wave's chunks");
   constexpr int NB = CPW / U;
@@ -110,7 +110,7 @@ SVG_DEV void stream_tiles_resident(P& p, int ntiles, int first, int stride, Pre&
   __builtin_amdgcn_sched_barrier(0);
   gate();
   typename P::template Acts<CPW> acts;
-  p.template load_acts<CPW, LDS>(acts, sb);
+  p.template load_acts<CPW, LDS, AUX>(acts, sb);
   TileSteps<P, CPW, U, 0, LDS>::run(p, b0, b1, acts, t, tn, ntiles, sb);
   p.finish(t, 0);
   // Two tiles per iteration: with an odd number of batches per tile the next
@@ -130,14 +130,14 @@ SVG_DEV void stream_tiles_resident(P& p, int ntiles, int first, int stride, Pre&
   }
 }
 
-template <class P, bool LDS>
+template <class P, bool LDS, int AUX>
 SVG_DEV void stream_tiles_simple(P& p, int ntiles, int first, int stride, int sb, int se) {
   int slot = 0;
   for (int t = first; t < ntiles; t += stride) {
     for (int j = sb; j < se; ++j) {
       typename P::template Acts<1> acts;
       typename P::template Batch<1> b;
-      p.template load_acts<1, LDS>(acts, j);
+      p.template load_acts<1, LDS, AUX>(acts, j);
       p.template load<1>(b, t, j, true);
       p.template compute<1, 0>(b, acts, t, j);
     }
@@ -146,11 +146,12 @@ SVG_DEV void stream_tiles_simple(P& p, int ntiles, int first, int stride, int sb
   }
 }
 
-template <class P, int WAVES, int CPW, int U, bool LDS = false, class Pre, class Gate>
+// AUX: cache policy of the activation loads from global memory
+template <class P, int WAVES, int CPW, int U, bool LDS = false, int AUX = 0, class Pre, class Gate>
 SVG_DEV void stream_tiles(P& p, const LinArgs& a, int first, int stride, Pre&& pre, Gate&& gate) {
   const int ntiles = (a.N + kTileRows - 1) / kTileRows;
   if constexpr (CPW > 0) {
-    stream_tiles_resident<P, CPW, U, LDS>(p, ntiles, first, stride, pre, gate);
+    stream_tiles_resident<P, CPW, U, LDS, AUX>(p, ntiles, first, stride, pre, gate);
   } else {
     if (first >= ntiles) return;
     pre();
@@ -158,7 +159,7 @@ SVG_DEV void stream_tiles(P& p, const LinArgs& a, int first, int stride, Pre&& p
     const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
     const int per = (KT + WAVES - 1) / WAVES;
     const int sb = min(KT, p.wave * per);
-    stream_tiles_simple<P, LDS>(p, ntiles, first, stride, sb, min(KT, sb + per));
+    stream_tiles_simple<P, LDS, AUX>(p, ntiles, first, stride, sb, min(KT, sb + per));
   }
 }
 
@@ -182,9 +183,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear(LinArgs a) {
 // The MFMA policies are not fused (measured, M = 2..4, in-launch
 // quantization into LDS cost 6 to 10 us per launch against 4 to 6 us for a
 // launch of its own: the weight stream stalls while every workgroup
-// quantizes).  Publishing the rows from a few workgroups to the others
-// inside one launch was measured slower too: the publishers' loads of X
-// queue behind the other workgroups' weight stream, and the readers' polls.
+// quantizes).  Publishing the rows from M workgroups to the others inside one
+// launch (k_linear_shared below) works but was measured slower than the
+// quantization launch too: at M = 16, K = 4096 the publishers are done about
+// 2.8 us after the launch starts and the readers see the last row about 5 us
+// in, a hand-off that costs more than a launch boundary.
 constexpr int kLdsMaxK = 12288;
 template <class P>
 constexpr int fused_rows() { return P::kMaxTok <= 2 ? P::kMaxTok : 0; }
@@ -192,7 +195,8 @@ constexpr int fused_rows() { return P::kMaxTok <= 2 ? P::kMaxTok : 0; }
 struct ActIn {
   const float* X;
   const int8_t* signs;
-  int block;  // transform block, 32 or 64
+  int block;          // transform block, 32 or 64
+  u32* ws = nullptr;  // the launch's workspace for shared quantization (k_linear_shared), if any
 };
 
 template <class P, int WAVES, int CPW, int U>
@@ -260,6 +264,78 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   });
 }
 
+// ------------------------------------------------- shared activation input
+// The rows of a verify batch (M >= 2, or a row too long for the fused
+// kernel's LDS), quantized once per launch instead of in a launch of their
+// own: workgroup m (m < M) rotates and quantizes row m into xq / x_scale and
+// counts it in; every workgroup waits until all M rows are in before it
+// reads its activation operands.  The last workgroup to finish zero-fills the
+// counters for the next call.  Workspace words (zero-filled before first
+// use): 1 rows counted in, 2 workgroups finished, 3 give-up flag (sticky: set
+// if the bounded wait ran out; then y is undefined).
+template <class P, int WAVES, int CPW, int U>
+__global__ __launch_bounds__(WAVES * 64) void k_linear_shared(LinArgs a, ActIn f) {
+  constexpr int CPT = WAVES >= 16 ? 3 : (WAVES >= 12 ? 4 : 2);
+  __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
+  __shared__ float act_red[16];
+  __shared__ float xsl[P::kMaxTok];
+  P p;
+  p.template init<WAVES>(a, red);
+  u32* ws = f.ws;
+  // Coherence across XCCs without cache maintenance: the publishers write the
+  // codes and scales through to memory (sc1 stores, then a wait for their
+  // acknowledgement) before counting them in; readers load them with sc1
+  // loads, which bypass the XCC's L2 -- a line of xq cached there by an
+  // earlier call would otherwise be read stale.
+  // Publishers are the workgroups with the lowest indices: workgroups are
+  // dispatched in index order, so a running workgroup's publishers have been
+  // dispatched too (running or done) -- no wait depends on one that is not.
+  // A publisher quantizes before it requests any weights; every workgroup
+  // requests its first weight batch before it waits for the rows, so that
+  // batch streams in meanwhile.
+  const int G = gridDim.x, bid = blockIdx.x;
+  stream_tiles<P, WAVES, CPW, U, false, kSC1>(p, a, bid, G, [&] {
+    if (bid < a.M) {
+      auto quantize = [&](auto block) {
+        constexpr int B = decltype(block)::value;
+        for (int m = bid; m < a.M; m += G)
+          act_quant_row<CPT, StoreGlobalT<kSC1>, B>(f.X + (size_t)m * a.K, a.K, f.signs,
+                                                    StoreGlobalT<kSC1>(const_cast<int8_t*>(a.xq), a.m0 + m, a.ldm,
+                                                                       const_cast<float*>(a.x_scale) + m, a.K),
+                                                    act_red);
+      };
+      if (f.block == 64) quantize(std::integral_constant<int, 64>{});
+      else quantize(std::integral_constant<int, 32>{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's codes and scale are performed
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(ws + 1, (u32)((a.M - bid + G - 1) / G), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }, [&] {
+    if (threadIdx.x == 0) {
+      for (u32 it = 0; __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (u32)a.M; ++it) {
+        if (it > (1u << 22)) {  // about a second: give up rather than hang
+          __hip_atomic_store(ws + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < a.M && (int)threadIdx.x < P::kMaxTok)
+      xsl[threadIdx.x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          make_rsrc(a.x_scale, (u32)a.M * 4u), threadIdx.x * 4u, 0, kSC1));
+    __syncthreads();
+    p.x_scale = xsl;
+  });
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(ws + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+    __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Workgroups resident on the device at once for a kernel (cached per kernel:
 // its occupancy is fixed when it is built).
 template <auto KERNEL>
@@ -283,10 +359,16 @@ int spread_grid(int ntiles, int block) {
   return std::max(1, (ntiles + rounds - 1) / rounds);
 }
 
-// f != nullptr (GEMV policies only): the fused kernel.
+// f != nullptr: the input rows are fp32 -- with a workspace, the shared
+// kernel; else (GEMV policies only) the fused kernel.
 template <class P, int WAVES, int CPW, int U>
 hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int ntiles = (a.N + kTileRows - 1) / kTileRows;
+  if (f && f->ws) {
+    constexpr auto kernel = k_linear_shared<P, WAVES, CPW, U>;
+    hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream, a, *f);
+    return hipGetLastError();
+  }
   if constexpr (fused_rows<P>() > 0) {
     if (f) {
       constexpr auto kernel = k_linear_fused<P, WAVES, CPW, U>;
@@ -316,7 +398,13 @@ hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 template <class P>
 hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
-  if (f && (a.M > fused_rows<P>() || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
+  ActIn fs;
+  if (f && f->ws) {  // with a workspace: quantize inside the launch, once, shared (M >= 2 or a long row)
+    fs = *f;
+    if (a.M <= fused_rows<P>() && a.K <= kLdsMaxK) fs.ws = nullptr;  // the fused kernel does better
+    f = &fs;
+  }
+  if (f && !f->ws && (a.M > fused_rows<P>() || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
     hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, f->block, const_cast<int8_t*>(a.xq),
                                             const_cast<float*>(a.x_scale), stream);
     if (e != hipSuccess) return e;

@@ -214,7 +214,7 @@ svg_status w4a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (st != SVG_OK) return st;
   if (M == 0 || N == 0) return ok();
   return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
-                                        group, N, y, partials_debug, nullptr, nullptr, 32,
+                                        group, N, y, partials_debug, nullptr, nullptr, 32, nullptr,
                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -226,14 +226,13 @@ svg_status w8a8_linear(const int8_t* xq, const float* x_scale, int M, int K, con
   if (st != SVG_OK) return st;
   if (M == 0 || N == 0) return ok();
   return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, nullptr,
-                                        nullptr, 32, reinterpret_cast<hipStream_t>(stream)));
+                                        nullptr, 32, nullptr, reinterpret_cast<hipStream_t>(stream)));
 }
 
-svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
-                                 int8_t* xq, float* x_scale, const uint8_t* wq, const uint16_t* w_scale,
-                                 const void* w_zero, int fmt, int group, int N, float* y,
-                                 int32_t* partials_debug, void* stream) {
-  static const char* fn = "act_quant_w4a8_linear";
+static svg_status fused_w4(const char* fn, const float* X, int M, int K, const int8_t* signs, int block,
+                           int8_t* xq, float* x_scale, const uint8_t* wq, const uint16_t* w_scale,
+                           const void* w_zero, int fmt, int group, int N, float* y, int32_t* partials_debug,
+                           uint32_t* ws, void* stream) {
   svg_status st = check_w4(fn, xq, x_scale, M, K, wq, w_scale, w_zero, fmt, group, N, y, partials_debug);
   if (st == SVG_OK) st = check_fused_input(fn, X, signs, block, K);
   if (st != SVG_OK) return st;
@@ -241,20 +240,61 @@ svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* sig
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, block, xq, x_scale, s));
   return hip_status(fn, svg_launch_w4a8(xq, x_scale, M, K, wq, w_scale, w_zero, fmt == SVG_W4_ASYM_Z4,
-                                        group, N, y, partials_debug, X, signs, block, s));
+                                        group, N, y, partials_debug, X, signs, block, ws, s));
 }
 
-svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
-                                 int8_t* xq, float* x_scale, const int8_t* wq, const uint16_t* w_scale,
-                                 int N, float* y, int32_t* partials_debug, void* stream) {
-  static const char* fn = "act_quant_w8a8_linear";
+static svg_status fused_w8(const char* fn, const float* X, int M, int K, const int8_t* signs, int block,
+                           int8_t* xq, float* x_scale, const int8_t* wq, const uint16_t* w_scale, int N, float* y,
+                           int32_t* partials_debug, uint32_t* ws, void* stream) {
   svg_status st = check_w8(fn, xq, x_scale, M, K, wq, w_scale, N, y, partials_debug);
   if (st == SVG_OK) st = check_fused_input(fn, X, signs, block, K);
   if (st != SVG_OK) return st;
   if (M == 0) return ok();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (N == 0) return hip_status(fn, svg_launch_act_rht_quant(X, M, K, signs, block, xq, x_scale, s));
-  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, X, signs, block, s));
+  return hip_status(fn, svg_launch_w8a8(xq, x_scale, M, K, wq, w_scale, N, y, partials_debug, X, signs, block, ws, s));
+}
+
+static svg_status check_linear_ws(const char* fn, const void* workspace) {
+  if (!workspace) return fail(SVG_EINVAL, fn, "null workspace");
+  if (!aligned(workspace, 256)) return fail(SVG_EALIGN, fn, "workspace needs 256-byte alignment");
+  return SVG_OK;
+}
+
+svg_status act_quant_w4a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
+                                 int8_t* xq, float* x_scale, const uint8_t* wq, const uint16_t* w_scale,
+                                 const void* w_zero, int fmt, int group, int N, float* y,
+                                 int32_t* partials_debug, void* stream) {
+  return fused_w4("act_quant_w4a8_linear", X, M, K, signs, block, xq, x_scale, wq, w_scale, w_zero, fmt, group,
+                  N, y, partials_debug, nullptr, stream);
+}
+
+svg_status act_quant_w8a8_linear(const float* X, int M, int K, const int8_t* signs, int block,
+                                 int8_t* xq, float* x_scale, const int8_t* wq, const uint16_t* w_scale,
+                                 int N, float* y, int32_t* partials_debug, void* stream) {
+  return fused_w8("act_quant_w8a8_linear", X, M, K, signs, block, xq, x_scale, wq, w_scale, N, y, partials_debug,
+                  nullptr, stream);
+}
+
+svg_status act_quant_w4a8_linear_ws(const float* X, int M, int K, const int8_t* signs, int block,
+                                    int8_t* xq, float* x_scale, const uint8_t* wq, const uint16_t* w_scale,
+                                    const void* w_zero, int fmt, int group, int N, float* y,
+                                    int32_t* partials_debug, void* workspace, void* stream) {
+  static const char* fn = "act_quant_w4a8_linear_ws";
+  const svg_status st = check_linear_ws(fn, workspace);
+  if (st != SVG_OK) return st;
+  return fused_w4(fn, X, M, K, signs, block, xq, x_scale, wq, w_scale, w_zero, fmt, group, N, y, partials_debug,
+                  static_cast<uint32_t*>(workspace), stream);
+}
+
+svg_status act_quant_w8a8_linear_ws(const float* X, int M, int K, const int8_t* signs, int block,
+                                    int8_t* xq, float* x_scale, const int8_t* wq, const uint16_t* w_scale,
+                                    int N, float* y, int32_t* partials_debug, void* workspace, void* stream) {
+  static const char* fn = "act_quant_w8a8_linear_ws";
+  const svg_status st = check_linear_ws(fn, workspace);
+  if (st != SVG_OK) return st;
+  return fused_w8(fn, X, M, K, signs, block, xq, x_scale, wq, w_scale, N, y, partials_debug,
+                  static_cast<uint32_t*>(workspace), stream);
 }
 
 svg_status tree_accept_greedy(const float* logits, int T, int V, const int32_t* parent, const int32_t* draft,

@@ -29,7 +29,8 @@ def svg():
 
 def test_header_declares_the_entry_points():
     assert _header_functions() == sorted(
-        ["act_quant_w4a8_linear", "act_quant_w8a8_linear", "act_rht_quant_i8", "rht_rotate_weights",
+        ["act_quant_w4a8_linear", "act_quant_w4a8_linear_ws", "act_quant_w8a8_linear", "act_quant_w8a8_linear_ws",
+         "act_rht_quant_i8", "rht_rotate_weights",
          "svg_export_act_codes", "svg_export_weights", "svg_import_act_codes", "svg_import_weights",
          "svg_last_error", "svg_pass_plan", "svg_pass_run", "svg_weight_sizes", "tree_accept_greedy", "tree_accept_greedy_static",
          "tree_deltanet_commit",
@@ -380,3 +381,17 @@ def test_act_layout_calls_validate_before_any_launch(svg, name):
     args = (A, 2, 64, rows_mis) if name == "svg_export_act_codes" else (rows_mis, 2, 64, A)
     assert fn(*args, NULL) == 3
     assert fn(A, 0, 64, A, NULL) == 0  # M = 0: nothing to do
+
+
+def test_workspace_calls_validate_the_workspace(svg):
+    """The _ws variants refuse a null or misaligned workspace before anything
+    else (pointers never dereferenced)."""
+    w4 = lambda ws: svg.lib.act_quant_w4a8_linear_ws(A, 2, 128, A, 32, A, A, A, A, A, 1, 64, 16, A, NULL,  # noqa: E731
+                                                      ws, NULL)
+    w8 = lambda ws: svg.lib.act_quant_w8a8_linear_ws(A, 2, 128, A, 32, A, A, A, A, 16, A, NULL, ws, NULL)  # noqa: E731
+    for fn in (w4, w8):
+        assert fn(NULL) == 1
+        assert fn(ctypes.c_void_p(0x10040)) == 3
+    # with a valid workspace the usual checks apply (here: M = 0 is a no-op)
+    assert svg.lib.act_quant_w4a8_linear_ws(A, 0, 128, A, 32, A, A, A, A, A, 1, 64, 16, A, NULL, A, NULL) == 0
+    assert svg.lib.act_quant_w4a8_linear_ws(A, 2, 128, A, 32, NULL, A, A, A, A, 1, 64, 16, A, NULL, A, NULL) == 1
