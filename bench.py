@@ -808,6 +808,28 @@ def main():
         print(f"[bench] linears alone per layer: M=1 {t1:.2f} us, M={M} {t16:.2f} us (x{t16 / t1:.3f})",
               file=sys.stderr, flush=True)
         del g1
+    if not args.no_configs and stack.engine == "launches" and args.workload != "stack_w8" and not args.unfused:
+        # the same passes as one persistent launch each (svg_pass_run: every
+        # linear a step that waits for all earlier ones)
+        res = {"description": "the pass as one launch of dependent steps (svg_pass_plan / svg_pass_run)"}
+        stack.engine = "pass"
+        try:
+            for m in ([1, M] if M != 1 else [1]):
+                if not stack.uses_pass(m):
+                    continue
+                io_p = stack.make_inputs(m)
+                g_p = stack.capture(io_p)
+                ms_p, med_p, _mn = time_graph(torch, g_p, args.steps, args.warmup, dev)
+                nb = stack.pass_bytes(m)
+                res[f"m{m}"] = {"ms_per_pass": round(ms_p, 5), "ms_per_pass_median": round(med_p, 5),
+                                "GB_per_s": round(nb / (ms_p * 1e-3) / 1e9, 2)}
+                print(f"[bench] one-launch pass M={m}: {ms_p:.4f} ms/pass", file=sys.stderr, flush=True)
+                del g_p, io_p
+        except RuntimeError as e:  # a bounded wait gave up: no timing
+            res["error"] = str(e)
+        finally:
+            stack.engine = "launches"
+        out["engine_pass"] = res
     if not args.no_configs and args.workload == "stack_w4g64":
         # the other configurations of the stack, timed in the same run: W8 at
         # its verify batch, and the g128 stack over the verify batch sizes

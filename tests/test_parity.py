@@ -561,14 +561,15 @@ def test_fused_in_captured_graph():
 
 # ------------------------------------------------- full-size stack launches
 # every launch kind of the timed passes (W4 g64 at M = 16 and 1, W8 at M = 32),
-# and the g128 sweep's M values
+# the g128 sweep's M values, and more two-row launches
 STACK_CASES = [("stack_w4g64", 16, "qkv"), ("stack_w4g64", 16, "o"), ("stack_w4g64", 16, "gateup"),
                ("stack_w4g64", 16, "down"), ("stack_w4g64", 1, "qkv"), ("stack_w4g64", 1, "o"),
                ("stack_w4g64", 1, "gateup"), ("stack_w4g64", 1, "down"), ("stack_w8", 32, "qkv"),
                ("stack_w8", 32, "o"), ("stack_w8", 32, "gateup"), ("stack_w8", 32, "down"),
                ("stack_w8", 1, "o"), ("stack_w4g128", 32, "down"), ("stack_w4g128", 32, "gateup"),
                ("stack_w4g128", 1, "qkv"), ("stack_w4g128", 2, "gateup"), ("stack_w4g128", 4, "down"),
-               ("stack_w4g128", 8, "o"), ("stack_w4g128", 16, "qkv")]
+               ("stack_w4g128", 8, "o"), ("stack_w4g128", 16, "qkv"), ("stack_w4g128", 2, "down"),
+               ("stack_w4g64", 2, "qkv")]
 
 
 @pytest.mark.parametrize("workload,M,launch", STACK_CASES)
@@ -607,12 +608,13 @@ def test_stack_launch_sampled_rows(workload, M, launch):
     assert np.array_equal(C.host(y2).view(np.uint32), yh.view(np.uint32))
 
 
-@pytest.mark.parametrize("workload,M", [("stack_w4g64", 16), ("stack_w8", 32)])
+@pytest.mark.parametrize("workload,M", [("stack_w4g64", 16), ("stack_w8", 32), ("stack_w4g128", 2)])
 def test_stack_o_launch_every_output(workload, M):
     """The o projection of the stack (4096 x 4096) at the verify batch of its
     format, issued as bench.py issues it, against the oracle on EVERY output:
     the per-group partial sums of all M x 4096 outputs bit-exact and all of y
-    within tolerance (one full-size launch of each matrix-core policy)."""
+    within tolerance (one full-size launch of each matrix-core policy; the
+    two-row launch pads a 16-row MFMA tile)."""
     spec = synth.WORKLOADS[workload]
     fmt, group = spec["fmt"], spec["group"]
     w, Ws, signs, space = C.stack_launch(0, "o", fmt, group)
