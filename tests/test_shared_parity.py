@@ -1,7 +1,7 @@
 """GPU parity of the fused calls with a workspace (act_quant_w4a8_linear_ws /
 act_quant_w8a8_linear_ws), whose verify-batch rows are rotated and quantized
-inside the linear's own launch by the first workgroups to start, through the
-C ABI, against the CPU oracle:
+inside the linear's own launch by workgroups 0 .. M-1 (each publishing its
+rows to the others), through the C ABI, against the CPU oracle:
 
  * activation codes and scales bit-exact, per-group partials bit-exact, y
    within 2e-3 of the fp64 reference;
