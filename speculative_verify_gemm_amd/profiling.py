@@ -96,9 +96,11 @@ def _first_arg(inner):
     return inner.rstrip(">")
 
 
-def trace_summary(d, cmd, only=None):
+def trace_summary(d, cmd, only=None, bench_json=None):
     """Per-kernel span statistics of a kernel trace; `only`: keep the kernels
-    whose name starts with it (the others are counted as other kernels)."""
+    whose name starts with it (the others are counted as other kernels).
+    With the traced run's bench.py output, the kernel digest it printed and
+    the figures of its JSON line that the trace cross-checks."""
     rows = _rows(d, "kernel_trace.csv")
     by, other = {}, []
     for r in rows:
@@ -113,7 +115,17 @@ def trace_summary(d, cmd, only=None):
             wgs *= max(1, g // w)
             wg *= w
         by.setdefault((n, wgs, wg), []).append(dur)
-    lines = ["# rocprofv3 kernel trace", "", "Command:", "", "```", cmd, "```", "",
+    head = []
+    if bench_json:
+        b = _bench_line(bench_json)
+        head = [f"digest: {b['kernel_digest']}", ""]
+        if "roofline" in b:
+            r = b["roofline"]
+            head[-1:] = [f"bench line of the traced run (timed under the profiler, which stretches the "
+                         f"event spans; the trace's own spans are below): {b['ms_per_step']} ms per pass "
+                         f"(M = {b['config'].get('M')}), mean linear launch {r.get('mean_launch_us')} us "
+                         f"({r.get('kernel')})", ""]
+    lines = ["# rocprofv3 kernel trace", "", "Command:", "", "```", cmd, "```", ""] + head + [
              "Durations are kernel-trace spans (start to end of each dispatch).", "",
              "| kernel | workgroups x threads | dispatches | mean us | median us | min us |",
              "|---|---|---|---|---|---|"]
@@ -328,6 +340,7 @@ def main(argv=None):
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--only", default=None, help="keep the kernels whose name starts with this")
+    t.add_argument("--bench-json", default=None, help="bench.py output of the traced run (digest, figures)")
     mf = sub.add_parser("mfma")
     mf.add_argument("runs", nargs="+", help="<counter dir>=<bench.py output of a plain run, same workload and M>")
     mf.add_argument("--cmd", required=True)
@@ -356,7 +369,7 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.what == "trace":
-        text = trace_summary(a.dir, a.cmd, a.only)
+        text = trace_summary(a.dir, a.cmd, a.only, a.bench_json)
     elif a.what == "hbm":
         text = hbm_summary(a.plain, a.trace_dir, a.cmd, a.reps)
     elif a.what == "calib":

@@ -77,6 +77,14 @@ def test_trace_summary_pools_the_linear_shapes(tmp_path):
     assert "| `k_linear<MfmaW4<1, 64, false, false>, 16, 6, 2>` | 256 x 1024 | 1 | 10.00 |" in text
     assert "`k_linear<MfmaW4<1, 64, false, false>>`: 3 dispatches, mean 6.667 us, median 6.000 us" in text
     assert "Other kernels (torch weight generation and fills at set-up): 1 dispatches, 2.0 ms in total." in text
+    # with the traced run's bench output: its kernel digest and headline figures
+    bj = tmp_path / "bench.json"
+    bj.write_text("[bench] noise\n" + json.dumps({
+        "kernel_digest": "00ff00ff00ff00ff", "ms_per_step": 1.8, "config": {"M": 16},
+        "roofline": {"mean_launch_us": 9.5, "kernel": "k_linear<MfmaW4<1, 64, false, false>, ...>"}}) + "\n")
+    text = P.trace_summary(str(tmp_path / "t"), "cmd", bench_json=str(bj))
+    assert "digest: 00ff00ff00ff00ff" in text
+    assert "1.8 ms per pass (M = 16), mean linear launch 9.5 us" in text
 
 
 def test_traffic_summary_scales_by_the_copy(tmp_path):
