@@ -216,6 +216,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   const int LT = min((int)blockDim.x, (nchunk + 64 * kLoadCPT - 1) / (64 * kLoadCPT) * 64);
   const bool row_early = R == 1 && nchunk <= LT * kLoadCPT;
   RowRegs<kLoadCPT> early;
+  // One row on the resident walk: every wave requests just the part of the
+  // row its own chunks cover (OWN_V values from k = wave * OWN_V), rotates it,
+  // and after one workgroup-wide maximum writes its codes to its own stretch
+  // of the LDS row and reads its operands back -- no barrier between codes and
+  // operands, since no other wave reads that stretch.
+  constexpr bool kOwn = R == 1 && CPW > 0 && WAVES * CPW * P::kChunkK <= kLdsMaxK;
+  constexpr int OWN_V = CPW * P::kChunkK;                // values per wave
+  constexpr int OWN_CPT = kOwn ? (OWN_V / 4 + 63) / 64 : 1;  // float4 chunks per lane
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int own_k0 = wave * OWN_V;
+  const int own_k = kOwn ? max(0, min(OWN_V, a.K - own_k0)) : 0;  // real values of this wave's part
+  RowRegs<OWN_CPT> own;
   __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
   __shared__ float act_red[16 * R];
   __shared__ __align__(16) u32 xl[R * kLdsMaxK / 4];
@@ -224,8 +236,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   p.template init<WAVES>(a, red);
   const int KP = ((a.K + 127) >> 7) * 32;  // words per LDS row: K padded to whole 128-k chunks
   stream_tiles<P, WAVES, CPW, U, true>(p, a, blockIdx.x, gridDim.x, [&] {
-    if (row_early && (int)threadIdx.x < LT) act_load_row<kLoadCPT>(f.X, a.K, f.signs, early, threadIdx.x, LT);
+    if constexpr (kOwn) {
+      // past its real values a part reads zeros (the resource ends there)
+      act_load_row<OWN_CPT>(f.X + own_k0, own_k, f.signs + own_k0, own, (u32)lane, 64u);
+    } else {
+      if (row_early && (int)threadIdx.x < LT) act_load_row<kLoadCPT>(f.X, a.K, f.signs, early, threadIdx.x, LT);
+    }
   }, [&] {
+    if constexpr (kOwn) {
+      auto quantize = [&](auto block) {
+        constexpr int B = decltype(block)::value;
+        const float amax = wg_max_once(act_rotate_loaded<OWN_CPT, B>(own), act_red);
+        u32* wl = xl + own_k0 / 4;
+        act_store_codes<OWN_CPT, StoreLds, B>(own, own_k, amax, StoreLds{wl, xsl}, (u32)lane, 64u);
+        for (int c = own_k / 4 + lane; c < OWN_V / 4; c += 64) wl[c] = 0u;  // k past K
+      };
+      if (f.block == 64) quantize(std::integral_constant<int, 64>{});
+      else quantize(std::integral_constant<int, 32>{});
+      if (blockIdx.x == 0) {  // the call's xq / x_scale outputs, each wave its part
+        for (int c = lane; c < own_k / 4; c += 64) {
+          const int w = own_k0 / 4 + c;  // word w (k = 4w) of the row
+          reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[((w >> 3) * a.ldm + a.m0) * 8 + (w & 7)] =
+              xl[w];
+        }
+        if (threadIdx.x == 0) const_cast<float*>(a.x_scale)[0] = xsl[0];
+      }
+      // the operand reads below must follow this wave's own LDS writes
+      asm volatile("" ::: "memory");
+    } else {
     // zero the padding (rows past M, k past K), quantize the rows.  (All
     // waves reading the rows before their weights was measured slower: the
     // start of the whole weight stream waits for the rows.)
@@ -257,6 +295,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
             xl[m * KP + w];
       }
       if (threadIdx.x < a.M) const_cast<float*>(a.x_scale)[threadIdx.x] = xsl[threadIdx.x];
+    }
     }
     p.xlds = reinterpret_cast<const int8_t*>(xl);
     p.xlds_row = KP * 4;
