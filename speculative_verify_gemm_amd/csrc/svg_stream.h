@@ -203,35 +203,40 @@ template <class P, int WAVES, int CPW, int U>
 __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f) {
   constexpr int R = fused_rows<P>();  // LDS rows
   static_assert(R > 0, "only the GEMV policies are fused");
-  // row chunks per thread held in registers: enough for every K the resident
-  // shapes of this size take (K <= 4096 with 8 waves, <= 12288 with 12 or
-  // 16); a longer row falls back to one row at a time
-  constexpr int CPT = WAVES >= 16 ? 3 : (WAVES >= 12 ? 4 : 2);
-  // One row (R == 1): only as many leading waves as hold the row with kLoadCPT
-  // chunks per lane request it, before their weights; the other waves request
-  // weights first.  Loads complete in order, so this keeps the row's latency
-  // off the weight stream of most waves and the weights' off the row.
-  constexpr int kLoadCPT = 4;
-  const int nchunk = a.K >> 2;
-  const int LT = min((int)blockDim.x, (nchunk + 64 * kLoadCPT - 1) / (64 * kLoadCPT) * 64);
-  const bool row_early = R == 1 && nchunk <= LT * kLoadCPT;
-  RowRegs<kLoadCPT> early;
-  // One row on the resident walk: every wave requests just the part of the
-  // row its own chunks cover (OWN_V values from k = wave * OWN_V), rotates it,
-  // and after one workgroup-wide maximum writes its codes to its own stretch
-  // of the LDS row and reads its operands back -- no barrier between codes and
-  // operands, since no other wave reads that stretch.
+  // How the row(s) get quantized.
+  //  * One row on the resident walk (kOwn): every wave requests just the part
+  //    of the row its own chunks cover (OWN_V values from k = wave * OWN_V)
+  //    before its weights, rotates it, joins one workgroup-wide maximum, and
+  //    writes its codes to its own stretch of the LDS row, from which it reads
+  //    its operands back -- no barrier between codes and operands, since no
+  //    other wave reads that stretch.
+  //  * Otherwise (two rows, or the plain walk): one row is held by as many
+  //    leading waves as hold it with kLoadCPT chunks per lane, requested
+  //    before their weights while the other waves request weights first
+  //    (row_early); two rows, or a row too long for that, are quantized by
+  //    the whole workgroup after its first weight batches (CPT chunks per
+  //    thread per row in registers: enough for every K the resident shapes of
+  //    this size take -- K <= 4096 with 8 waves, <= 12288 with 12 or 16 --
+  //    and longer rows one at a time).  The codes go to the shared LDS rows
+  //    (zero-padded) and a barrier precedes the operand reads.
   constexpr bool kOwn = R == 1 && CPW > 0 && WAVES * CPW * P::kChunkK <= kLdsMaxK;
-  constexpr int OWN_V = CPW * P::kChunkK;                // values per wave
+  constexpr int OWN_V = CPW * P::kChunkK;                    // values per wave
   constexpr int OWN_CPT = kOwn ? (OWN_V / 4 + 63) / 64 : 1;  // float4 chunks per lane
+  constexpr int CPT = WAVES >= 16 ? 3 : (WAVES >= 12 ? 4 : 2);
+  constexpr int kLoadCPT = 4;
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
   const int own_k0 = wave * OWN_V;
   const int own_k = kOwn ? max(0, min(OWN_V, a.K - own_k0)) : 0;  // real values of this wave's part
+  const int nchunk = a.K >> 2;
+  const int LT = min((int)blockDim.x, (nchunk + 64 * kLoadCPT - 1) / (64 * kLoadCPT) * 64);
+  const bool row_early = !kOwn && R == 1 && nchunk <= LT * kLoadCPT;
   RowRegs<OWN_CPT> own;
+  RowRegs<kLoadCPT> early;
   __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
   __shared__ float act_red[16 * R];
   __shared__ __align__(16) u32 xl[R * kLdsMaxK / 4];
   __shared__ float xsl[R];
+  __shared__ float own_scale[WAVES];  // each wave's copy of the row scale (wave 0's is xsl)
   P p;
   p.template init<WAVES>(a, red);
   const int KP = ((a.K + 127) >> 7) * 32;  // words per LDS row: K padded to whole 128-k chunks
@@ -243,12 +248,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
       if (row_early && (int)threadIdx.x < LT) act_load_row<kLoadCPT>(f.X, a.K, f.signs, early, threadIdx.x, LT);
     }
   }, [&] {
+    // the transform block is uniform over the launch: both forms are in the
+    // kernel and one branch picks
     if constexpr (kOwn) {
       auto quantize = [&](auto block) {
         constexpr int B = decltype(block)::value;
         const float amax = wg_max_once(act_rotate_loaded<OWN_CPT, B>(own), act_red);
         u32* wl = xl + own_k0 / 4;
-        act_store_codes<OWN_CPT, StoreLds, B>(own, own_k, amax, StoreLds{wl, xsl}, (u32)lane, 64u);
+        act_store_codes<OWN_CPT, StoreLds, B>(own, own_k, amax, StoreLds{wl, wave == 0 ? xsl : own_scale + wave},
+                                              (u32)lane, 64u);
         for (int c = own_k / 4 + lane; c < OWN_V / 4; c += 64) wl[c] = 0u;  // k past K
       };
       if (f.block == 64) quantize(std::integral_constant<int, 64>{});
@@ -264,38 +272,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
       // the operand reads below must follow this wave's own LDS writes
       asm volatile("" ::: "memory");
     } else {
-    // zero the padding (rows past M, k past K), quantize the rows.  (All
-    // waves reading the rows before their weights was measured slower: the
-    // start of the whole weight stream waits for the rows.)
-    for (int i = threadIdx.x; i < R * KP; i += blockDim.x)
-      if (i / KP >= a.M || (i % KP) * 4 >= a.K) xl[i] = 0u;
-    // the transform block is uniform over the launch: both forms are in the
-    // kernel and one branch picks
-    auto quantize = [&](auto block) {
-      constexpr int B = decltype(block)::value;
-      if (row_early) {
-        const bool holds = (int)threadIdx.x < LT;
-        const float amax = wg_max_once(holds ? act_rotate_loaded<kLoadCPT, B>(early) : 0.f, act_red);
-        if (holds) act_store_codes<kLoadCPT, StoreLds, B>(early, a.K, amax, StoreLds{xl, xsl}, threadIdx.x, LT);
-      } else if (a.K <= 4 * CPT * (int)blockDim.x) {
-        act_quant_rows_lds<R, CPT, B>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
-      } else {
-        for (int m = 0; m < a.M; ++m)
-          act_quant_row<CPT, StoreLds, B>(f.X + (size_t)m * a.K, a.K, f.signs, StoreLds{xl + m * KP, xsl + m},
-                                          act_red);
+      for (int i = threadIdx.x; i < R * KP; i += blockDim.x)  // zero the padding (rows past M, k past K)
+        if (i / KP >= a.M || (i % KP) * 4 >= a.K) xl[i] = 0u;
+      auto quantize = [&](auto block) {
+        constexpr int B = decltype(block)::value;
+        if (row_early) {
+          const bool holds = (int)threadIdx.x < LT;
+          const float amax = wg_max_once(holds ? act_rotate_loaded<kLoadCPT, B>(early) : 0.f, act_red);
+          if (holds)
+            act_store_codes<kLoadCPT, StoreLds, B>(early, a.K, amax, StoreLds{xl, xsl}, threadIdx.x, LT);
+        } else if (a.K <= 4 * CPT * (int)blockDim.x) {
+          act_quant_rows_lds<R, CPT, B>(f.X, a.M, a.K, f.signs, xl, KP, xsl, act_red);
+        } else {
+          for (int m = 0; m < a.M; ++m)
+            act_quant_row<CPT, StoreLds, B>(f.X + (size_t)m * a.K, a.K, f.signs,
+                                            StoreLds{xl + m * KP, xsl + m}, act_red);
+        }
+      };
+      if (f.block == 64) quantize(std::integral_constant<int, 64>{});
+      else quantize(std::integral_constant<int, 32>{});
+      __syncthreads();
+      if (blockIdx.x == 0) {  // the call's xq / x_scale outputs
+        for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x) {
+          const int m = i / (a.K / 4), w = i % (a.K / 4);  // word w (k = 4w) of row m
+          reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[((w >> 3) * a.ldm + a.m0 + m) * 8 + (w & 7)] =
+              xl[m * KP + w];
+        }
+        if (threadIdx.x < a.M) const_cast<float*>(a.x_scale)[threadIdx.x] = xsl[threadIdx.x];
       }
-    };
-    if (f.block == 64) quantize(std::integral_constant<int, 64>{});
-    else quantize(std::integral_constant<int, 32>{});
-    __syncthreads();
-    if (blockIdx.x == 0) {  // the call's xq / x_scale outputs
-      for (int i = threadIdx.x; i < a.M * (a.K / 4); i += blockDim.x) {
-        const int m = i / (a.K / 4), w = i % (a.K / 4);  // word w (k = 4w) of row m
-        reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[((w >> 3) * a.ldm + a.m0 + m) * 8 + (w & 7)] =
-            xl[m * KP + w];
-      }
-      if (threadIdx.x < a.M) const_cast<float*>(a.x_scale)[threadIdx.x] = xsl[threadIdx.x];
-    }
     }
     p.xlds = reinterpret_cast<const int8_t*>(xl);
     p.xlds_row = KP * 4;
