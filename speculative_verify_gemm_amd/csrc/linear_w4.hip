@@ -162,6 +162,10 @@ struct MfmaW4 : W4Common {
   static_assert(G == 64 || G == 128, "MFMA path handles groups of 64 and 128");
   static constexpr int kChunkK = 128, kActRegs = 8 * MH, kRedRows = MH * 16, kMaxTok = 16 * MH;
   static constexpr int kBatchRegs = 6, kFixedRegs = 48;
+  // verify batches are quantized in a launch of their own (in the linear's
+  // launch they were measured slower: the rows' registers leave one
+  // workgroup per CU)
+  static constexpr int kFusedRows = 0;
   static constexpr int GPC = 128 / G;  // groups per 128-k chunk
   using red_t = float;
   template <int NC>
@@ -282,6 +286,7 @@ struct MfmaW4 : W4Common {
 template <int MT, int G, bool Z4, bool DBG>
 struct DotW4 : W4Common {
   static constexpr int kChunkK = 128, kActRegs = 8 * MT, kRedRows = MT, kMaxTok = MT;
+  static constexpr int kFusedRows = MT <= 2 ? MT : 0;  // rows a launch quantizes itself
   static constexpr int kBatchRegs = 6, kFixedRegs = 48;
   static constexpr int GPC = 128 / G;
   using red_t = float;

@@ -83,6 +83,7 @@ struct W8Common {
 template <int MT>
 struct DotW8 : W8Common {
   static constexpr int kChunkK = 64, kActRegs = 4 * MT, kRedRows = MT, kMaxTok = MT;
+  static constexpr int kFusedRows = MT <= 2 ? MT : 0;  // rows a launch quantizes itself
   static constexpr int kBatchRegs = 4, kFixedRegs = 36;
   using red_t = int;
   template <int NC>
@@ -155,6 +156,7 @@ struct DotW8 : W8Common {
 template <int MH>
 struct MfmaW8 : W8Common {
   static constexpr int kChunkK = 64, kActRegs = 4 * MH, kRedRows = MH * 16, kMaxTok = 16 * MH;
+  static constexpr int kFusedRows = 0;  // verify batches are quantized in a launch of their own
   static constexpr int kBatchRegs = 4, kFixedRegs = 36;
   using red_t = int;
   template <int NC>

@@ -180,17 +180,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear(LinArgs a) {
 // workgroups.  Workgroup 0 also writes xq and x_scale (the values
 // act_rht_quant_i8 gives).  K <= kLdsMaxK.
 //
-// The MFMA policies are not fused (measured, M = 2..4, in-launch
-// quantization into LDS cost 6 to 10 us per launch against 4 to 6 us for a
-// launch of its own: the weight stream stalls while every workgroup
-// quantizes).  Publishing the rows from M workgroups to the others inside one
+// The MFMA policies are not fused: measured at M = 2..4, first with whole
+// rows quantized by the whole workgroup (6 to 10 us per launch against 4 to
+// 6 us for a launch of its own), then with each wave quantizing its own
+// stretch of every row (the g128 stack's M = 2 and 4 passes 10 and 15 %
+// slower than with the quantization launch: the rows' registers leave one
+// workgroup per CU).  Publishing the rows from M workgroups to the others inside one
 // launch (k_linear_shared below) works but was measured slower than the
 // quantization launch too: at M = 16, K = 4096 the publishers are done about
 // 2.8 us after the launch starts and the readers see the last row about 5 us
 // in, a hand-off that costs more than a launch boundary.
 constexpr int kLdsMaxK = 12288;
 template <class P>
-constexpr int fused_rows() { return P::kMaxTok <= 2 ? P::kMaxTok : 0; }
+constexpr int fused_rows() { return P::kFusedRows; }
 
 struct ActIn {
   const float* X;
@@ -204,13 +206,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   constexpr int R = fused_rows<P>();  // LDS rows
   static_assert(R > 0, "only the GEMV policies are fused");
   // How the row(s) get quantized.
-  //  * One row on the resident walk (kOwn): every wave requests just the part
-  //    of the row its own chunks cover (OWN_V values from k = wave * OWN_V)
-  //    before its weights, rotates it, joins one workgroup-wide maximum, and
-  //    writes its codes to its own stretch of the LDS row, from which it reads
-  //    its operands back -- no barrier between codes and operands, since no
-  //    other wave reads that stretch.
-  //  * Otherwise (two rows, or the plain walk): one row is held by as many
+  //  * On the resident walk (kOwn): every wave requests just the part of each
+  //    row its own chunks cover (OWN_V values from k = wave * OWN_V) before
+  //    its weights, rotates it, joins one workgroup-wide maximum per row, and
+  //    writes its codes to its own stretch of the LDS rows (row stride: all
+  //    waves' stretches), from which it reads its operands back -- no barrier
+  //    between codes and operands, since no other wave reads that stretch.
+  //  * Otherwise (the plain walk, or shapes wider than LDS): one row is held by as many
   //    leading waves as hold it with kLoadCPT chunks per lane, requested
   //    before their weights while the other waves request weights first
   //    (row_early); two rows, or a row too long for that, are quantized by
@@ -219,9 +221,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   //    this size take -- K <= 4096 with 8 waves, <= 12288 with 12 or 16 --
   //    and longer rows one at a time).  The codes go to the shared LDS rows
   //    (zero-padded) and a barrier precedes the operand reads.
-  constexpr bool kOwn = R == 1 && CPW > 0 && WAVES * CPW * P::kChunkK <= kLdsMaxK;
+  constexpr bool kOwn = CPW > 0 && WAVES * CPW * P::kChunkK <= kLdsMaxK;
   constexpr int OWN_V = CPW * P::kChunkK;                    // values per wave
   constexpr int OWN_CPT = kOwn ? (OWN_V / 4 + 63) / 64 : 1;  // float4 chunks per lane
+  constexpr int OWN_ROW = WAVES * OWN_V / 4;                 // LDS words per row
   constexpr int CPT = WAVES >= 16 ? 3 : (WAVES >= 12 ? 4 : 2);
   constexpr int kLoadCPT = 4;
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
@@ -230,20 +233,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
   const int nchunk = a.K >> 2;
   const int LT = min((int)blockDim.x, (nchunk + 64 * kLoadCPT - 1) / (64 * kLoadCPT) * 64);
   const bool row_early = !kOwn && R == 1 && nchunk <= LT * kLoadCPT;
-  RowRegs<OWN_CPT> own;
+  RowRegs<OWN_CPT> own[R];
   RowRegs<kLoadCPT> early;
   __shared__ typename P::red_t red[2 * WAVES * P::kRedRows * kTileRows];
   __shared__ float act_red[16 * R];
   __shared__ __align__(16) u32 xl[R * kLdsMaxK / 4];
   __shared__ float xsl[R];
-  __shared__ float own_scale[WAVES];  // each wave's copy of the row scale (wave 0's is xsl)
+  __shared__ float own_scale[WAVES * R];  // each wave's copy of the row scales (wave 0's is xsl)
   P p;
   p.template init<WAVES>(a, red);
   const int KP = ((a.K + 127) >> 7) * 32;  // words per LDS row: K padded to whole 128-k chunks
   stream_tiles<P, WAVES, CPW, U, true>(p, a, blockIdx.x, gridDim.x, [&] {
     if constexpr (kOwn) {
-      // past its real values a part reads zeros (the resource ends there)
-      act_load_row<OWN_CPT>(f.X + own_k0, own_k, f.signs + own_k0, own, (u32)lane, 64u);
+      // past its real values a part reads zeros (the resource ends there);
+      // rows past M read nothing
+#pragma unroll
+      for (int m = 0; m < R; ++m)
+        act_load_row<OWN_CPT>(f.X + (size_t)m * a.K + own_k0, m < a.M ? own_k : 0, f.signs + own_k0, own[m],
+                              (u32)lane, 64u);
     } else {
       if (row_early && (int)threadIdx.x < LT) act_load_row<kLoadCPT>(f.X, a.K, f.signs, early, threadIdx.x, LT);
     }
@@ -253,21 +260,33 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
     if constexpr (kOwn) {
       auto quantize = [&](auto block) {
         constexpr int B = decltype(block)::value;
-        const float amax = wg_max_once(act_rotate_loaded<OWN_CPT, B>(own), act_red);
-        u32* wl = xl + own_k0 / 4;
-        act_store_codes<OWN_CPT, StoreLds, B>(own, own_k, amax, StoreLds{wl, wave == 0 ? xsl : own_scale + wave},
-                                              (u32)lane, 64u);
-        for (int c = own_k / 4 + lane; c < OWN_V / 4; c += 64) wl[c] = 0u;  // k past K
+        float amax[R];
+#pragma unroll
+        for (int m = 0; m < R; ++m) amax[m] = act_rotate_loaded<OWN_CPT, B>(own[m]);
+        if constexpr (R == 1) amax[0] = wg_max_once(amax[0], act_red);
+        else wg_max_rows<R>(amax, act_red);
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+          u32* wl = xl + m * OWN_ROW + own_k0 / 4;
+          const int real = m < a.M ? own_k : 0;
+          if (real > 0)
+            act_store_codes<OWN_CPT, StoreLds, B>(own[m], real, amax[m],
+                                                  StoreLds{wl, wave == 0 ? xsl + m : own_scale + wave * R + m},
+                                                  (u32)lane, 64u);
+          for (int c = real / 4 + lane; c < OWN_V / 4; c += 64) wl[c] = 0u;  // k past K, rows past M
+        }
       };
       if (f.block == 64) quantize(std::integral_constant<int, 64>{});
       else quantize(std::integral_constant<int, 32>{});
       if (blockIdx.x == 0) {  // the call's xq / x_scale outputs, each wave its part
-        for (int c = lane; c < own_k / 4; c += 64) {
-          const int w = own_k0 / 4 + c;  // word w (k = 4w) of the row
-          reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[((w >> 3) * a.ldm + a.m0) * 8 + (w & 7)] =
-              xl[w];
-        }
-        if (threadIdx.x == 0) const_cast<float*>(a.x_scale)[0] = xsl[0];
+        for (int m = 0; m < a.M; ++m)
+          for (int c = lane; c < own_k / 4; c += 64) {
+            const int w = own_k0 / 4 + c;  // word w (k = 4w) of row m
+            reinterpret_cast<u32*>(const_cast<int8_t*>(a.xq))[((w >> 3) * a.ldm + a.m0 + m) * 8 + (w & 7)] =
+                xl[m * OWN_ROW + w];
+          }
+        if (threadIdx.x == 0)
+          for (int m = 0; m < a.M; ++m) const_cast<float*>(a.x_scale)[m] = xsl[m];
       }
       // the operand reads below must follow this wave's own LDS writes
       asm volatile("" ::: "memory");
@@ -302,7 +321,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_fused(LinArgs a, ActIn f)
       }
     }
     p.xlds = reinterpret_cast<const int8_t*>(xl);
-    p.xlds_row = KP * 4;
+    p.xlds_row = (kOwn ? OWN_ROW : KP) * 4;
     p.x_scale = xsl;
   });
 }
@@ -413,23 +432,30 @@ int spread_grid(int ntiles, int block) {
   return G;
 }
 
-// f != nullptr: the input rows are fp32 -- with a workspace, the shared
-// kernel; else (GEMV policies only) the fused kernel.
+// f != nullptr: the input rows are fp32.  Calls of at most fused_rows<P>()
+// rows take the fused kernel; otherwise, with a workspace, the shared kernel;
+// else the rows are quantized in a launch of their own first.
 template <class P, int WAVES, int CPW, int U>
 hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int ntiles = (a.N + kTileRows - 1) / kTileRows;
-  if (f && f->ws) {
-    constexpr auto kernel = k_linear_shared<P, WAVES, CPW, U>;
-    hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream, a, *f);
-    return hipGetLastError();
-  }
-  if constexpr (fused_rows<P>() > 0) {
-    if (f) {
-      constexpr auto kernel = k_linear_fused<P, WAVES, CPW, U>;
+  if (f) {
+    if constexpr (fused_rows<P>() > 0) {
+      if (a.M <= fused_rows<P>() && a.K <= kLdsMaxK) {
+        constexpr auto kernel = k_linear_fused<P, WAVES, CPW, U>;
+        hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream,
+                           a, *f);
+        return hipGetLastError();
+      }
+    }
+    if (f->ws) {
+      constexpr auto kernel = k_linear_shared<P, WAVES, CPW, U>;
       hipLaunchKernelGGL(kernel, dim3(spread_grid<kernel>(ntiles, WAVES * 64)), dim3(WAVES * 64), 0, stream,
                          a, *f);
       return hipGetLastError();
     }
+    hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, f->block, const_cast<int8_t*>(a.xq),
+                                            const_cast<float*>(a.x_scale), stream);
+    if (e != hipSuccess) return e;
   }
   {
     constexpr auto kernel = k_linear<P, WAVES, CPW, U>;
@@ -452,18 +478,6 @@ hipError_t launch_linear(const LinArgs& a, const ActIn* f, hipStream_t stream) {
 template <class P>
 hipError_t launch_linear_auto(const LinArgs& a, const ActIn* f, hipStream_t stream) {
   const int KT = (a.K + P::kChunkK - 1) / P::kChunkK;
-  ActIn fs;
-  if (f && f->ws) {  // with a workspace: quantize inside the launch, once, shared (M >= 2 or a long row)
-    fs = *f;
-    if (a.M <= fused_rows<P>() && a.K <= kLdsMaxK) fs.ws = nullptr;  // the fused kernel does better
-    f = &fs;
-  }
-  if (f && !f->ws && (a.M > fused_rows<P>() || a.K > kLdsMaxK)) {  // not fusable: quantize in a launch of their own
-    hipError_t e = svg_launch_act_rht_quant(f->X, a.M, a.K, f->signs, f->block, const_cast<int8_t*>(a.xq),
-                                            const_cast<float*>(a.x_scale), stream);
-    if (e != hipSuccess) return e;
-    f = nullptr;
-  }
 #define SVG_FITS(CPW, U, LIM) (P::kActRegs * (CPW) + 2 * (U) * P::kBatchRegs + P::kFixedRegs <= (LIM))
 #define SVG_TRY(W, CPW, U, LIM) \
   if constexpr (SVG_FITS(CPW, U, LIM)) return launch_linear<P, W, CPW, U>(a, f, stream)
