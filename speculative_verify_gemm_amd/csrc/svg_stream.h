@@ -376,7 +376,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_linear_shared(LinArgs a, ActIn f
   }, [&] {
     if (threadIdx.x == 0) {
       for (u32 it = 0; __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (u32)a.M; ++it) {
-        if (it > (1u << 22)) {  // about a second: give up rather than hang
+        if (it > (1u << 20)) {  // about a second of device-scope polls: give up rather than hang
           __hip_atomic_store(ws + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
