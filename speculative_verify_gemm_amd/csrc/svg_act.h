@@ -57,8 +57,7 @@ SVG_DEV void act_codes4(const float u[4], float sigma, float rinv, bool fast, in
 // Max over the workgroup with one barrier, for a `red` (>= 16 floats of LDS)
 // that no earlier code of the kernel reads.
 SVG_DEV float wg_max_once(float v, float* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  v = wave_max(v);
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
@@ -69,8 +68,7 @@ SVG_DEV float wg_max_once(float v, float* red) {
 
 // Max over the workgroup (exact: max is order-free).  red: >= 16 floats of LDS.
 SVG_DEV float wg_max(float v, float* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  v = wave_max(v);
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   __syncthreads();  // red may still be read by a previous call
   if ((threadIdx.x & 63) == 0) red[wave] = v;
@@ -196,9 +194,7 @@ template <int R>
 SVG_DEV void wg_max_rows(float (&v)[R], float* red) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v[r] = fmaxf(v[r], __shfl_xor(v[r], off));
+  for (int r = 0; r < R; ++r) v[r] = wave_max(v[r]);
   __syncthreads();  // red may still be read by a previous call
   if ((threadIdx.x & 63) == 0)
 #pragma unroll

@@ -37,6 +37,22 @@ SVG_DEV int lane_xor(int v) {
 template <int MASK>
 SVG_DEV float lane_xorf(float v) { return __int_as_float(lane_xor<MASK>(__float_as_int(v))); }
 
+// Maximum over the wave, the same in every lane, with no LDS access: DPP
+// inside each quad and each row of 16 lanes (row rotations by 4 and 8), then
+// the four rows' values read out as scalars.  Exact (max is order-free).
+SVG_DEV float wave_max(float v) {
+  v = fmaxf(v, lane_xorf<1>(v));
+  v = fmaxf(v, lane_xorf<2>(v));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // ------------------------------------------- 32-wide Walsh-Hadamard butterfly
 // A block of 32 values is spread over 8 consecutive lanes, 4 consecutive
 // values per lane (lane j of the block holds elements 4j..4j+3).  Stages run
