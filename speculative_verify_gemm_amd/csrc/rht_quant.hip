@@ -72,8 +72,9 @@ __global__ __launch_bounds__(NT) void k_act_rht_quant(const float* __restrict__ 
                                                      int8_t* __restrict__ xq, float* __restrict__ x_scale) {
   __shared__ float red[16];
   const int m = blockIdx.x;
-  act_quant_row<CPT, StoreGlobal, B>(X + (size_t)m * K, K, signs, StoreGlobal(xq, m, gridDim.x, x_scale + m, K),
-                                     red);
+  // one row per workgroup: `red` serves one maximum only
+  act_quant_row<CPT, StoreGlobal, B, true>(X + (size_t)m * K, K, signs,
+                                           StoreGlobal(xq, m, gridDim.x, x_scale + m, K), red);
 }
 
 // Group-wise min/max over the LPG = G/4 lanes that hold one quantization group.

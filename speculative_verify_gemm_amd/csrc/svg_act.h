@@ -183,9 +183,11 @@ SVG_DEV void act_store_codes(const RowRegs<CPT>& r, int K, float amax, const Sto
 
 // Rotate and quantize a row loaded by act_load_row (K <= 4 * NT * CPT); codes
 // and the scale go to `st`.  Every thread of the workgroup must call it.
-template <int CPT, class Store, int B = 32>
+// ONCE: the kernel's only use of `red` (one barrier fewer).
+template <int CPT, class Store, int B = 32, bool ONCE = false>
 SVG_DEV void act_quant_loaded(RowRegs<CPT>& r, int K, const Store& st, float* red) {
-  const float amax = wg_max(act_rotate_loaded<CPT, B>(r), red);
+  const float v = act_rotate_loaded<CPT, B>(r);
+  const float amax = ONCE ? wg_max_once(v, red) : wg_max(v, red);
   act_store_codes<CPT, Store, B>(r, K, amax, st);
 }
 
@@ -231,13 +233,13 @@ SVG_DEV void act_quant_rows_lds(const float* X, int M, int K, const int8_t* sign
 // scale go to `st`.  Every thread of the workgroup must call it.  The row is
 // held in registers when K <= 4 * NT * CPT (one read of the input); longer
 // rows are read twice (the second pass recomputes the same rotated values).
-template <int CPT, class Store, int B = 32>
+template <int CPT, class Store, int B = 32, bool ONCE = false>
 SVG_DEV void act_quant_row(const float* x, int K, const int8_t* signs, const Store& st, float* red) {
   const u32 NT = blockDim.x, nchunk = (u32)K >> 2;
   if (nchunk <= NT * CPT) {
     RowRegs<CPT> r;
     act_load_row<CPT>(x, K, signs, r);
-    act_quant_loaded<CPT, Store, B>(r, K, st, red);
+    act_quant_loaded<CPT, Store, B, ONCE>(r, K, st, red);
     return;
   }
   const rsrc_t xr = make_rsrc(x, (u32)K * 4u);
@@ -248,7 +250,7 @@ SVG_DEV void act_quant_row(const float* x, int K, const int8_t* signs, const Sto
     act_rotate4<B>(xr, sr, c, e);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3]))));
   }
-  amax = wg_max(amax, red);
+  amax = ONCE ? wg_max_once(amax, red) : wg_max(amax, red);
   const float sigma = amax / 127.0f;
   const float rinv = 1.0f / sigma;
   const bool fast = sigma >= 0x1p-125f;
