@@ -68,6 +68,10 @@ __global__ __launch_bounds__(kThreads) void k_tree_accept(const float* __restric
                                                          u64* keys, u32* row_count, u32* rows_done) {
   __shared__ u64 wave_best[kThreads / 64];
   __shared__ int last;
+  // every argument in one round trip (else the slice bounds wait for S and L
+  // before the rest is requested)
+  asm volatile("" ::"s"(logits), "s"(T), "s"(V), "s"(S), "s"(L), "s"(parent), "s"(draft), "s"(target), "s"(path),
+               "s"(emit), "s"(n_emit), "s"(keys), "s"(row_count), "s"(rows_done));
 
   // ---- 1. slice maximum
   const int row = blockIdx.x / S, s = blockIdx.x % S;

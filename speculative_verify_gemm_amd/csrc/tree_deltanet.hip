@@ -118,6 +118,14 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_verify(const float* __res
   __shared__ Tokens<DK, DV> tok;
   const int node = blockIdx.x, h = blockIdx.y, row0 = blockIdx.z * kRowsPerGroup;
   const int rl = threadIdx.x / Lo::TPR, r = row0 + rl, c0 = (threadIdx.x % Lo::TPR) * Lo::EPT;
+  // the state rows do not depend on the path: requested before its walk
+  float S[Lo::EPT];
+  const float* s0 = state + ((size_t)h * DV + r) * DK + c0;
+#pragma unroll
+  for (int c = 0; c < Lo::EPT; c += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(s0 + c);
+    S[c] = t.x; S[c + 1] = t.y; S[c + 2] = t.z; S[c + 3] = t.w;
+  }
   if (threadIdx.x == 0) {  // the root path, root first; -1 if it is not a tree path
     int n = node, d = 0, ok = 1;
     int rev[kMaxNodes];
@@ -137,13 +145,6 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_verify(const float* __res
   if (len < 0) {  // malformed tree: the node's output is NaN
     if (c0 == 0) out[((size_t)node * H + h) * DV + r] = __builtin_nanf("");
     return;
-  }
-  float S[Lo::EPT];
-  const float* s0 = state + ((size_t)h * DV + r) * DK + c0;
-#pragma unroll
-  for (int c = 0; c < Lo::EPT; c += 4) {
-    const float4 t = *reinterpret_cast<const float4*>(s0 + c);
-    S[c] = t.x; S[c + 1] = t.y; S[c + 2] = t.z; S[c + 3] = t.w;
   }
   stage_tokens<DK, DV>(path, len, k, v, alpha, beta, H, h, row0, tok);
   for (int j = 0; j < len; ++j)
@@ -176,6 +177,15 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_commit(float* __restrict_
   __shared__ Tokens<DK, DV> tok;
   const int h = blockIdx.x, row0 = blockIdx.y * kRowsPerGroup;
   const int rl = threadIdx.x / Lo::TPR, r = row0 + rl, c0 = (threadIdx.x % Lo::TPR) * Lo::EPT;
+  // this thread's part of the state rows, requested before the accepted path
+  // is read (only this thread writes it back)
+  float S[Lo::EPT];
+  float* s0 = state + ((size_t)h * DV + r) * DK + c0;
+#pragma unroll
+  for (int c = 0; c < Lo::EPT; c += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(s0 + c);
+    S[c] = t.x; S[c + 1] = t.y; S[c + 2] = t.z; S[c + 3] = t.w;
+  }
   if (threadIdx.x == 0) {  // root, then the accepted nodes; nothing if they are not valid nodes
     const int n = n_emit[0];
     int ok = n >= 1 && n <= T;
@@ -189,13 +199,6 @@ __global__ __launch_bounds__(kThreads) void k_gdn_tree_commit(float* __restrict_
   }
   __syncthreads();
   if (len == 0) return;
-  float S[Lo::EPT];
-  float* s0 = state + ((size_t)h * DV + r) * DK + c0;
-#pragma unroll
-  for (int c = 0; c < Lo::EPT; c += 4) {
-    const float4 t = *reinterpret_cast<const float4*>(s0 + c);
-    S[c] = t.x; S[c + 1] = t.y; S[c + 2] = t.z; S[c + 3] = t.w;
-  }
   stage_tokens<DK, DV>(nodes, len, k, v, alpha, beta, H, h, row0, tok);
   for (int j = 0; j < len; ++j)
     gdn_advance<Lo::TPR, Lo::EPT>(S, tok.k + j * DK, tok.v[j * kRowsPerGroup + rl], tok.a[j], tok.b[j], c0);
