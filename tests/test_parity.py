@@ -608,18 +608,22 @@ def test_stack_launch_sampled_rows(workload, M, launch):
     assert np.array_equal(C.host(y2).view(np.uint32), yh.view(np.uint32))
 
 
-@pytest.mark.parametrize("workload,M", [("stack_w4g64", 16), ("stack_w8", 32), ("stack_w4g128", 2)])
-def test_stack_o_launch_every_output(workload, M):
-    """The o projection of the stack (4096 x 4096) at the verify batch of its
-    format, issued as bench.py issues it, against the oracle on EVERY output:
-    the per-group partial sums of all M x 4096 outputs bit-exact and all of y
-    within tolerance (one full-size launch of each matrix-core policy; the
-    two-row launch pads a 16-row MFMA tile)."""
+@pytest.mark.parametrize("workload,M,launch", [("stack_w4g64", 16, "o"), ("stack_w8", 32, "o"),
+                                               ("stack_w4g128", 2, "o"), ("stack_w4g64", 16, "down"),
+                                               ("stack_w4g64", 1, "down")])
+def test_stack_launch_every_output(workload, M, launch):
+    """A projection of the stack -- o (4096 x 4096) at the verify batch of
+    each format, down (4096 x 12288, the 16-wave x 6-chunk shape) at 16 rows
+    and at one row (quantized inside the launch) -- issued as bench.py issues
+    it, against the oracle on EVERY output: the per-group partial sums of all
+    M x 4096 outputs bit-exact and all of y within tolerance (one full-size
+    launch of each matrix-core policy; the two-row launch pads a 16-row MFMA
+    tile)."""
     spec = synth.WORKLOADS[workload]
     fmt, group = spec["fmt"], spec["group"]
-    w, Ws, signs, space = C.stack_launch(0, "o", fmt, group)
+    w, Ws, signs, space = C.stack_launch(0, launch, fmt, group)
     N, K = w["N"], w["K"]
-    C.say(f"stack o launch, every output: {workload} M={M} N={N} K={K}")
+    C.say(f"stack {launch} launch, every output: {workload} M={M} N={N} K={K}")
     x = synth.stack_acts(workload, 0, space, M)
     xq, xs, y, dbg = C.gpu_fused(x, signs, w)
     W = C.stacked_rows(Ws, list(range(N)))
